@@ -1,0 +1,226 @@
+"""Throughput of the fused SSIM loss, forward + backward, fp32, on one MI355X.
+
+One step = ssim_forward (training mode: loss + saved maps) followed by
+ssim_backward (both image gradients) on one batch of synthetic images already
+resident in HBM, through the C ABI on torch's current stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: metric Mpix/s (pixels = N*H*W per step), the roofline
+of the dominant kernel (algorithmic bytes per launch / average launch time
+from HIP events recorded around every launch of the timed region), and the
+fp64 CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PAGES_MPIX_S = 1920 * 1080 / 7.2e-3 / 1e6  # the pages' 7.2 ms fwd+bwd at 1080p (RDNA4 R9700)
+KERNEL_SRC = os.path.join(ROOT, "ssim_loss_amd", "csrc", "ssim_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="1080p-valid")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps timed with a cache flush before each (0 = skip)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(shape, padding):
+    """Compulsory HBM bytes per launch of each kernel (saved-maps design):
+    forward reads x, y (8 B per input element) and writes four fp32 maps
+    (16 B per map entry); backward reads the maps (16 B per entry), x and y
+    (8 B per element) and writes both gradients (8 B per element)."""
+    N, C, H, W = shape
+    Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
+    e_in = N * C * H * W
+    e_out = N * C * Ho * Wo
+    return {"ssim_forward": 8 * e_in + 16 * e_out, "ssim_backward": 16 * e_out + 16 * e_in}
+
+
+def cpu_baseline(x, y, padding, pixels_per_image_batch):
+    """The fp64 oracle, as it stands, on the host cores: whole forward +
+    gradient of the same workload, repeated until about 10 s have passed
+    (at most 4 times)."""
+    import oracle
+
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    threads = max(1, min(16, ncores))
+    oracle.set_threads(threads)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ssim_loss(x, y, padding)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 4:
+            break
+    return {
+        "value": round(reps * pixels_per_image_batch / el / 1e6, 3),
+        "unit": "Mpix/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{reps} x whole forward+gradient of the benchmark batch "
+                  f"({x.shape}, {padding}) in {el:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by image planes with one scalar all-reduce, which is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ssim_loss_amd as S
+    from ssim_loss_amd.inputs import WORKLOADS, make_workload
+
+    w = WORKLOADS[args.workload]
+    x, y = make_workload(args.workload)
+    N, C, H, W = x.shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t1 = torch.from_numpy(x).to(dev)
+    t2 = torch.from_numpy(y).to(dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    maps = S.alloc_saved_maps(t1, w.padding)
+    ws = S.workspace_for(dev)
+    dloss = torch.tensor(0.8, dtype=torch.float32, device=dev)  # as under a weighted loss
+    g1 = torch.empty_like(t1)
+    g2 = torch.empty_like(t2)
+    torch.cuda.synchronize()
+
+    def step():
+        S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
+        S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
+        ev[k][1].record()
+        S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = elapsed * 1e3 / K
+    mpix = N * H * W / 1e6
+    value = mpix * K / elapsed
+
+    # cold: flush the 256 MB last-level cache before each step (outside the events)
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        cf, cb = [], []
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
+            e[1].record()
+            S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+            e[2].record()
+            torch.cuda.synchronize()
+            cf.append(e[0].elapsed_time(e[1]))
+            cb.append(e[1].elapsed_time(e[2]))
+        del flush
+        cold = {"fwd_ms": round(sum(cf) / len(cf), 5), "bwd_ms": round(sum(cb) / len(cb), 5),
+                "mpix_per_s": round(mpix / ((sum(cf) + sum(cb)) / len(cf) / 1e3), 1)}
+
+    if args.copy_calib > 0:
+        n = args.copy_calib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    alg = algorithmic_bytes((N, C, H, W), w.padding)
+    kern = {"ssim_forward": fwd_ms, "ssim_backward": bwd_ms}
+    dom = max(kern, key=kern.get)
+    achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if (tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload
+                and dom in tr.get("bytes_per_launch", {})):
+            traffic = tr["bytes_per_launch"][dom]
+
+    out = {
+        "metric": "Mpix/s fused SSIM fwd+bwd fp32 at 1080p; achieved HBM GB/s as % of peak",
+        "value": round(value, 1),
+        "unit": "Mpix/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_MPIX_S, 2) if args.workload == "1080p-valid" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "shape": [N, C, H, W], "padding": w.padding},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg[dom],
+        },
+        "kernels_ms": {"ssim_forward": round(fwd_ms, 5), "ssim_backward": round(bwd_ms, 5)},
+        "step_hbm_gbs": round((alg["ssim_forward"] + alg["ssim_backward"]) /
+                              ((fwd_ms + bwd_ms) * 1e-3) / 1e9, 1),
+        "cold": cold,
+        "loss": float(loss.item()),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x, y, w.padding, N * H * W)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * ssim_loss_amd.h -- C ABI of the fused SSIM loss (forward + backward) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The loss is  loss = 1 - mean SSIM  over every map entry of an NCHW batch
+ * ("TriSSIM -- A Highly Optimized Triton-based Fused SSIM Library", Usage:
+ * the train loss is one minus fused_ssim), where the SSIM map uses the 11x11
+ * Gaussian window of the original SSIM paper ("Fully Fused Differentiable
+ * SSIM", opening section: separable, symmetric, hard-coded weights; here
+ * sigma 1.5, taps normalised to sum 1), C1 = 0.01^2, C2 = 0.03^2 (images in
+ * [0,1]: "Fully Fused Differentiable SSIM", Constraints), and either "valid"
+ * or zero-filled "same" padding ("Fully Fused Differentiable SSIM", Usage).
+ * The backward applies the adjoint of the blur and the chain rule of
+ * "TriSSIM", How it works.
+ *
+ * Conventions shared by every entry point:
+ *   - Images, maps, gradients and loss are device pointers (HIP device
+ *     memory) owned by the caller.  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and completes asynchronously.
+ *   - Images are contiguous fp32 NCHW, N*C planes of H rows of W pixels.
+ *     img1 and img2 have the same shape.  Values are meant to lie in [0,1].
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Every argument check happens before any HIP call; a failed check
+ *     returns a negative code and enqueues nothing.  A launch failure
+ *     returns SSIM_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation, as HIP errors.  No C++ exception crosses the ABI.
+ *   - Calls are reentrant.  Concurrent calls (on different streams) need
+ *     distinct loss, saved_maps and workspace buffers.
+ */
+#ifndef SSIM_LOSS_AMD_H
+#define SSIM_LOSS_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSIM_ABI_VERSION 1
+
+/* padding ("Fully Fused Differentiable SSIM", Usage) */
+enum {
+  SSIM_PAD_VALID = 0, /* map is (H-10) x (W-10): windows inside the image only */
+  SSIM_PAD_SAME = 1   /* map is H x W: window centred, zeros outside the image */
+};
+
+/* return codes */
+enum {
+  SSIM_OK = 0,
+  SSIM_ERR_NULL = -1,     /* a required pointer is NULL */
+  SSIM_ERR_SHAPE = -2,    /* N, C, H or W <= 0, or valid padding with H < 11 or W < 11 */
+  SSIM_ERR_PADDING = -3,  /* padding is neither SSIM_PAD_VALID nor SSIM_PAD_SAME */
+  SSIM_ERR_OVERFLOW = -4, /* one plane (or one map plane) holds 2^31 or more elements,
+                             or a buffer size overflows size_t */
+  SSIM_ERR_ALIAS = -5,    /* an output buffer overlaps an input or another output */
+  SSIM_ERR_HIP = -6,      /* a HIP runtime call failed (launch, device query) */
+  SSIM_ERR_DEVICE = -7    /* the current device is not a wave64 gfx9 GPU */
+};
+
+/* Version of this ABI (SSIM_ABI_VERSION of the library that was built). */
+int ssim_abi_version(void);
+
+/* Static, human-readable text for a return code.  Never NULL. */
+const char* ssim_strerror(int code);
+
+/* The 11 one-dimensional Gaussian taps (fp32) the kernels use, copied to
+ * `out` (host memory, 11 floats).  g[k] is proportional to
+ * exp(-(k-5)^2 / (2 * 1.5^2)), normalised to sum 1, rounded once to fp32;
+ * the 2-D window is g g^T.  Host-only; touches no GPU. */
+void ssim_taps(float out[11]);
+
+/* Output (map) extent for an H x W image: valid gives (H-10) x (W-10),
+ * same gives H x W.  Returns SSIM_OK, or SSIM_ERR_SHAPE / SSIM_ERR_PADDING.
+ * Host-only. */
+int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo);
+
+/* Bytes of the saved-maps buffer ssim_forward writes in training mode and
+ * ssim_backward reads: four fp32 maps per plane, each Ho rows with a row
+ * pitch of Wo rounded up to a multiple of 4 floats, i.e.
+ * 16 * N*C * Ho * roundup(Wo, 4) bytes.  The buffer must be 16-byte
+ * aligned.  Returns 0 for invalid arguments.  Host-only. */
+size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding);
+
+/* Bytes of the workspace ssim_forward needs (a per-workgroup partial-sum
+ * table and a completion counter).  The caller zero-fills it once, before
+ * its first use; every ssim_forward leaves it ready for the next call (the
+ * last workgroup resets the counter).  One workspace must not be used by
+ * two ssim_forward calls that may run at the same time.  Host-only. */
+size_t ssim_workspace_bytes(void);
+
+/* Forward.  Computes loss = 1 - (1/M) * sum over the N*C*Ho*Wo map entries
+ * of SSIM, M = N*C*Ho*Wo, and writes it as one fp32 to `loss` (device).
+ *
+ *   img1, img2  : fp32 NCHW device images (inputs, not modified)
+ *   N, C, H, W  : shape; each plane must hold fewer than 2^31 elements
+ *   padding     : SSIM_PAD_VALID or SSIM_PAD_SAME
+ *   loss        : device fp32 scalar (output)
+ *   saved_maps  : NULL for inference (no gradient will be taken), else a
+ *                 device buffer of ssim_saved_maps_bytes(...) bytes that
+ *                 receives, at every map entry, the partial derivatives of
+ *                 the loss with respect to the four blurred quantities the
+ *                 kernels form -- B(x - 1/2), B(y - 1/2), B((x - y)^2) (times
+ *                 2) and B((x - 1/2)(y - 1/2)) -- as four planes per image
+ *                 plane; ssim_backward consumes them.
+ *   workspace   : device buffer of ssim_workspace_bytes() bytes, zeroed
+ *                 before its first use
+ *   stream      : hipStream_t (NULL = default stream)
+ *
+ * The reduction is deterministic: the same inputs give the same bits. */
+int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int64_t H,
+                 int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
+                 void* stream);
+
+/* Backward.  Writes grad_img1 = dloss * d loss / d img1 and
+ * grad_img2 = dloss * d loss / d img2 (fp32 NCHW, same shape as the images)
+ * by applying the adjoint of the blur to the saved maps and the chain rule
+ * ("TriSSIM", How it works).
+ *
+ *   dloss       : device fp32 scalar, the upstream gradient of the loss
+ *   img1, img2  : the images given to ssim_forward (unchanged since)
+ *   N..padding  : as given to ssim_forward
+ *   saved_maps  : the buffer ssim_forward filled (unchanged since)
+ *   grad_img1   : device output, or NULL to skip it
+ *   grad_img2   : device output, or NULL to skip it (both NULL: no-op)
+ *   stream      : hipStream_t (NULL = default stream) */
+int ssim_backward(const float* dloss, const float* img1, const float* img2, int64_t N,
+                  int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
+                  float* grad_img1, float* grad_img2, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSIM_LOSS_AMD_H */

@@ -1,0 +1,244 @@
+"""Fused SSIM loss (forward + backward) on AMD MI355X: thin Python binding.
+
+The C ABI (``include/ssim_loss_amd.h``) is the product; this module only
+marshals torch tensors into its pointers and sizes and calls it on torch's
+current HIP stream.  Every step of the computation runs in the HIP kernels of
+``libssim_loss_amd.so``; there is no fallback path.  If the library is
+missing, importing the functions below raises.
+
+Functions with the C names:
+  ssim_forward(img1, img2, padding, loss, saved_maps, workspace)
+  ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2)
+  ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
+  ssim_strerror, ssim_abi_version
+Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
+  ssim_loss(img1, img2, padding="valid", train=True) -> 1 - mean SSIM
+  fused_ssim(img1, img2, padding="same", train=True)  -> mean SSIM
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+PAD = {"valid": 0, "same": 1}
+SSIM_OK = 0
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SsimError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {ssim_strerror(code)} (code {code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -m ssim_loss_amd.build "
+                "or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.ssim_abi_version.restype = i32
+        L.ssim_abi_version.argtypes = []
+        L.ssim_strerror.restype = ctypes.c_char_p
+        L.ssim_strerror.argtypes = [i32]
+        L.ssim_taps.restype = None
+        L.ssim_taps.argtypes = [vp]
+        L.ssim_map_shape.restype = i32
+        L.ssim_map_shape.argtypes = [i64, i64, i32, vp, vp]
+        L.ssim_saved_maps_bytes.restype = sz
+        L.ssim_saved_maps_bytes.argtypes = [i64, i64, i64, i64, i32]
+        L.ssim_workspace_bytes.restype = sz
+        L.ssim_workspace_bytes.argtypes = []
+        L.ssim_forward.restype = i32
+        L.ssim_forward.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp, vp, vp]
+        L.ssim_backward.restype = i32
+        L.ssim_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _pad(padding) -> int:
+    if isinstance(padding, str):
+        if padding not in PAD:
+            raise ValueError(f"padding must be 'valid' or 'same', got {padding!r}")
+        return PAD[padding]
+    return int(padding)
+
+
+# --------------------------------------------------------------------------- host-only calls
+def ssim_abi_version() -> int:
+    return int(lib().ssim_abi_version())
+
+
+def ssim_strerror(code: int) -> str:
+    return lib().ssim_strerror(int(code)).decode()
+
+
+def ssim_taps() -> list[float]:
+    buf = (ctypes.c_float * 11)()
+    lib().ssim_taps(buf)
+    return list(buf)
+
+
+def ssim_map_shape(H: int, W: int, padding) -> tuple[int, int]:
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().ssim_map_shape(int(H), int(W), _pad(padding), ctypes.byref(ho), ctypes.byref(wo))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_map_shape")
+    return int(ho.value), int(wo.value)
+
+
+def ssim_saved_maps_bytes(N: int, C: int, H: int, W: int, padding) -> int:
+    return int(lib().ssim_saved_maps_bytes(int(N), int(C), int(H), int(W), _pad(padding)))
+
+
+def ssim_workspace_bytes() -> int:
+    return int(lib().ssim_workspace_bytes())
+
+
+# --------------------------------------------------------------------------- device calls
+def _stream_ptr(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_image(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor, got device {t.device}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be NCHW (4-D), got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous NCHW")
+
+
+def ssim_forward(img1, img2, padding, loss, saved_maps, workspace) -> None:
+    """Calls the C ``ssim_forward`` on torch's current stream.  All arguments
+    are preallocated device tensors (saved_maps may be None)."""
+    _check_image(img1, "img1")
+    _check_image(img2, "img2")
+    if img1.shape != img2.shape:
+        raise ValueError("img1 and img2 must have the same shape")
+    N, C, H, W = img1.shape
+    rc = lib().ssim_forward(_dptr(img1), _dptr(img2), N, C, H, W, _pad(padding), _dptr(loss),
+                            _dptr(saved_maps), _dptr(workspace), _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_forward")
+
+
+def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) -> None:
+    """Calls the C ``ssim_backward`` on torch's current stream."""
+    _check_image(img1, "img1")
+    _check_image(img2, "img2")
+    N, C, H, W = img1.shape
+    rc = lib().ssim_backward(_dptr(dloss), _dptr(img1), _dptr(img2), N, C, H, W, _pad(padding),
+                             _dptr(saved_maps), _dptr(grad_img1), _dptr(grad_img2),
+                             _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_backward")
+
+
+# --------------------------------------------------------------------------- buffers
+_workspaces: dict = {}
+
+
+def workspace_for(device) -> "torch.Tensor":
+    """A zero-initialised workspace per device, created once.  Calls that use
+    it must not overlap in time (one stream per device, as torch's default)."""
+    import torch
+
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros(ssim_workspace_bytes(), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
+def alloc_saved_maps(img1, padding) -> "torch.Tensor":
+    import torch
+
+    N, C, H, W = img1.shape
+    nbytes = ssim_saved_maps_bytes(N, C, H, W, padding)
+    if nbytes == 0:
+        raise SsimError(-2, "ssim_saved_maps_bytes")
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=img1.device)
+
+
+# --------------------------------------------------------------------------- autograd
+def _make_function():
+    import torch
+
+    class _SsimLoss(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, img1, img2, padding, train):
+            img1 = img1.detach()
+            img2 = img2.detach()
+            loss = torch.empty((), dtype=torch.float32, device=img1.device)
+            maps = alloc_saved_maps(img1, padding) if train else None
+            ssim_forward(img1, img2, padding, loss, maps, workspace_for(img1.device))
+            ctx.padding = padding
+            ctx.train = train
+            if train:
+                ctx.save_for_backward(img1, img2, maps)
+            return loss
+
+        @staticmethod
+        def backward(ctx, dloss):
+            if not ctx.train:
+                raise RuntimeError("ssim_loss was called with train=False; no gradient saved")
+            img1, img2, maps = ctx.saved_tensors
+            want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+            g1 = torch.empty_like(img1) if want1 else None
+            g2 = torch.empty_like(img2) if want2 else None
+            dl = dloss.detach().to(dtype=torch.float32).contiguous()
+            ssim_backward(dl, img1, img2, ctx.padding, maps, g1, g2)
+            return g1, g2, None, None
+
+    return _SsimLoss
+
+
+_fn = None
+
+
+def ssim_loss(img1, img2, padding: str = "valid", train: bool = True):
+    """loss = 1 - mean SSIM (a 0-d fp32 tensor on the images' device), with
+    gradients for whichever of img1 / img2 requires them."""
+    global _fn
+    if _fn is None:
+        _fn = _make_function()
+    _check_image(img1, "img1")
+    _check_image(img2, "img2")
+    if img1.shape != img2.shape:
+        raise ValueError("img1 and img2 must have the same shape")
+    _pad(padding)
+    return _fn.apply(img1, img2, padding, bool(train))
+
+
+def fused_ssim(img1, img2, padding: str = "same", train: bool = True):
+    """Mean SSIM ("Fully Fused Differentiable SSIM", Usage: default padding
+    "same")."""
+    return 1.0 - ssim_loss(img1, img2, padding, train)

@@ -1,0 +1,742 @@
+// ssim_kernels.hip -- fused SSIM loss, forward and backward, for gfx950.
+//
+// What is computed ("Fully Fused Differentiable SSIM", opening section and
+// Usage; "TriSSIM", How it works and Usage): the SSIM map of the 11x11
+// Gaussian window, loss = 1 - mean(map), and its gradient with respect to
+// both images through the adjoint B^T of the blur and the chain rule.
+//
+// Readings of the pages that keep the work and the rounding error down
+// without changing the result:
+//   * One blur pass serves several statistics ("Fully Fused Differentiable
+//     SSIM", opening section).  SSIM needs the second moments only through
+//     sigma_xy and sigma_x^2 + sigma_y^2 = 2 sigma_xy + var(x - y), so four
+//     blurred quantities suffice: mu_x' = B(x'), mu_y' = B(y'),
+//     P' = B(x' y') and R = B((x - y)^2), with x' = x - 1/2, y' = y - 1/2.
+//     Then, with dmu = mu_x - mu_y,
+//         A1 = 2 mu_x mu_y + C1,  D1 = dmu^2,            B1 = A1 + D1
+//         A2 = 2 (P' - mu_x' mu_y') + C2,  D2 = R - dmu^2, B2 = A2 + D2
+//         1 - S = (A1 D2 + D1 B2) / (B1 B2).
+//     The shift by 1/2 leaves every variance unchanged and halves the
+//     magnitudes that cancel in P' - mu_x' mu_y'; the difference basis makes
+//     B1 - A1 and B2 - A2 exact by construction, so identical images give a
+//     loss and gradients of exactly zero and near-identical images (SSIM
+//     near 1, the end of a training run) keep full relative accuracy in
+//     1 - S, which is what the loss sums.
+//   * The pages send five upstream gradients through B^T (mu1, mu2, s11, s22,
+//     s12); in the basis above there are four maps, m0..m3 = d loss /
+//     d(mu_x', mu_y', R, P') (R's with the chain rule's 2 folded in), and
+//         grad_x = dloss * (B^T m0 + y' * B^T m3 + (x - y) * B^T m2)
+//         grad_y = dloss * (B^T m1 + x' * B^T m3 - (x - y) * B^T m2).
+//   * The window is symmetric and B^T of a zero-filled correlation is a
+//     correlation with the same taps shifted by the padding; so forward and
+//     backward are one "blur with input offset" skeleton:
+//         out[i][j] = sum_{a,b} g[a] g[b] in[i + a - off][j + b - off],
+//     in = 0 outside its extent (for the forward: pixels x = y = 0 there, so
+//     x' = y' = -1/2 -- load-then-shift produces exactly that).  Forward:
+//     off = 0 (valid) or 5 (same); backward: off = 10 (valid: the "full"
+//     correlation) or 5 (same).
+//
+// Skeleton (one workgroup = 4 wave64 = 256 lanes; one strip = 256 input
+// columns -> 244 output columns):
+//   column pass : lane t owns input column j0 - off + t.  It marches down the
+//                 rows, loading its own pixel per row straight from HBM
+//                 (coalesced across lanes), and keeps the last 11 rows of the
+//                 four quantities in a 12-slot register ring; each new row
+//                 gives one column-blurred row of the four quantities.
+//   row pass    : batches of 4 column-blurred rows go through a double-
+//                 buffered LDS tile [quantity][row][256] (32 KiB); wave w then
+//                 takes row w of the batch and lane l produces the 4 adjacent
+//                 outputs 4l..4l+3 from 4 aligned 16-byte LDS reads per
+//                 quantity (conflict-free: lanes read consecutive 16 bytes).
+//   consumer    : forward -> SSIM, loss partial sum, 4 map stores (16 bytes
+//                 each, one per map plane); backward -> chain rule and two
+//                 gradient stores.
+// Work is split into (plane, strip, output row) units; each workgroup takes
+// an equal contiguous range of units (a persistent-style grid of about one
+// wave of resident workgroups), marching down its strips so that every
+// input row is loaded and column-blurred once per strip, plus a 10-row
+// warm-up where a range starts.  Workgroup ids are remapped so that each of
+// the 8 XCDs (separate L2s) owns one contiguous eighth of the units: strips
+// that share a 10-column halo then run side by side on the same L2.
+//
+// Loss reduction: the map entries of 1 - S are summed as per-lane fp32 sums
+// of 4 outputs -> fp64 per lane -> wave64 shuffle tree -> LDS -> one fp64
+// partial per workgroup -> the last workgroup (completion ticket) sums the
+// partials in a fixed order and writes loss = sum / M.  Deterministic; no
+// atomics on floating point.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "ssim_loss_amd.h"
+
+#if defined(__HIP_DEVICE_COMPILE__)
+#if !defined(__gfx950__)
+#error "this library targets gfx950 (MI355X) only"
+#endif
+#endif
+
+namespace {
+
+constexpr int kWave = 64;        // gfx9 wavefront size; checked on the host at run time
+constexpr int kThreads = 256;    // 4 waves per workgroup
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTileW = 256;      // input columns per strip: one per lane
+constexpr int kStripOut = 244;   // outputs per strip: 256 - 10, rounded down to a multiple of 4
+constexpr int kRowLanes = kStripOut / 4;  // lanes active in the row pass (61)
+constexpr int kRows = 4;         // rows per batch = waves (one row each in the row pass)
+constexpr int kRing = 12;        // ring slots: 11 rows needed, 12 so 3 batches of 4 close the cycle
+constexpr int kQ = 4;            // blurred quantities / maps
+constexpr int kMaxBlocks = 4096; // bound on the grid (size of the partial-sum table)
+constexpr int kMinRowsPerBlock = 8;
+
+static_assert(kRows == kWaves, "row pass maps one batch row per wave");
+static_assert(4 * (kRowLanes - 1) + 16 <= kTileW, "row-pass reads stay inside the tile");
+static_assert(kStripOut + 10 <= kTileW, "a strip's halo fits the tile");
+static_assert(kStripOut % 4 == 0, "strips start on 16-byte boundaries");
+
+// 1-D Gaussian taps: exp(-(k-5)^2 / (2 * 1.5^2)) normalised to sum 1 (the
+// original SSIM paper's window; "Fully Fused Differentiable SSIM" hard-codes
+// its weights), written out to 17 significant digits and rounded once to
+// fp32.  Symmetric: g[k] == g[10-k].
+constexpr float kTap0 = 0.0010283800844791100f;
+constexpr float kTap1 = 0.0075987581352391900f;
+constexpr float kTap2 = 0.036000772128430830f;
+constexpr float kTap3 = 0.10936068950970002f;
+constexpr float kTap4 = 0.21300553771125370f;
+constexpr float kTap5 = 0.26601172486179436f;
+
+__host__ __device__ constexpr float tap(int k) {
+  return (k == 0 || k == 10) ? kTap0
+       : (k == 1 || k == 9)  ? kTap1
+       : (k == 2 || k == 8)  ? kTap2
+       : (k == 3 || k == 7)  ? kTap3
+       : (k == 4 || k == 6)  ? kTap4
+                             : kTap5;
+}
+
+constexpr float kC1 = 1.0e-4f;  // (0.01 * 1)^2
+constexpr float kC2 = 9.0e-4f;  // (0.03 * 1)^2
+constexpr float kShift = 0.5f;  // x' = x - 1/2 (see the file header)
+
+struct Workspace {
+  unsigned int ticket;
+  unsigned int pad[63];
+  double partial[kMaxBlocks];
+};
+
+enum Mode { kFwdInfer = 0, kFwdTrain = 1, kBwd = 2 };
+
+struct Params {
+  // blur geometry
+  int in_h, in_w;       // extent of the blurred input (fwd: H x W, bwd: Ho x Wo)
+  int in_pitch;         // row pitch of the input planes, elements
+  int64_t in_plane;     // elements between consecutive planes of one input array
+  int out_h, out_w;     // output extent (fwd: Ho x Wo, bwd: H x W)
+  int off;              // in row = out row + a - off (same for columns)
+  int strips;           // ceil(out_w / kStripOut)
+  int64_t units;        // planes * strips * out_h
+  // images (fwd: the inputs; bwd: read by the chain rule)
+  const float* x;
+  const float* y;
+  int64_t img_plane;    // H * W
+  int img_w;            // W
+  // maps (fwd: written in training mode; bwd: the blurred input)
+  float* maps;
+  int map_pitch;        // roundup(Wo, 4)
+  int64_t map_plane;    // Ho * map_pitch
+  // forward
+  float k_m2;           // -2 / M
+  double inv_m;         // 1 / M
+  float* loss;
+  Workspace* ws;
+  // backward
+  const float* dloss;
+  float* gx;
+  float* gy;
+};
+
+// ---------------------------------------------------------------------------
+// Column loads and the quantities they feed
+
+template <int MODE>
+struct Raw;
+template <>
+struct Raw<kFwdInfer> { float v[2]; };
+template <>
+struct Raw<kFwdTrain> { float v[2]; };
+template <>
+struct Raw<kBwd> { float v[4]; };
+
+// Pixel (row r) of this lane's column; zero outside the input extent.
+template <int MODE>
+__device__ __forceinline__ void load_row(const Params& p, const float* __restrict__ c0,
+                                         const float* __restrict__ c1, bool col_ok, int r,
+                                         Raw<MODE>& out) {
+  const bool ok = col_ok && (unsigned)r < (unsigned)p.in_h;
+  if constexpr (MODE == kBwd) {
+    const int64_t o = (int64_t)r * p.in_pitch;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out.v[k] = ok ? c0[o + k * p.map_plane] : 0.0f;
+  } else {
+    const int o = r * p.in_pitch;
+    out.v[0] = ok ? c0[o] : 0.0f;
+    out.v[1] = ok ? c1[o] : 0.0f;
+  }
+}
+
+// Quantities blurred by the forward: x', y', (x - y)^2 and x' y' with
+// x' = x - 1/2, y' = y - 1/2.  The backward blurs its four maps as they are.
+template <int MODE>
+__device__ __forceinline__ void quantities(const Raw<MODE>& r, float (&q)[kQ]) {
+  if constexpr (MODE == kBwd) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = r.v[k];
+  } else {
+    const float x = r.v[0] - kShift, y = r.v[1] - kShift;
+    const float d = r.v[0] - r.v[1];
+    q[0] = x;
+    q[1] = y;
+    q[2] = d * d;
+    q[3] = x * y;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Consumers (4 adjacent outputs of one row)
+
+// 1 - SSIM and the four loss partials at one map position, from the blurred
+// quantities mu_x', mu_y', R = B((x-y)^2), P' = B(x' y').
+struct SsimOut {
+  float ell;   // 1 - S
+  float m[4];  // loss partials (training mode)
+};
+
+template <bool kTrain>
+__device__ __forceinline__ SsimOut ssim_point(float mxs, float mys, float rr, float pp,
+                                              float k_m2) {
+  SsimOut o;
+  const float mux = mxs + kShift, muy = mys + kShift;
+  const float dm = mxs - mys;
+  const float a1 = __builtin_fmaf(2.0f * mux, muy, kC1);
+  const float d1 = dm * dm;
+  const float b1 = a1 + d1;
+  const float cov = __builtin_fmaf(-mxs, mys, pp);
+  const float a2 = __builtin_fmaf(2.0f, cov, kC2);
+  const float d2 = __builtin_fmaf(-dm, dm, rr);
+  const float b2 = a2 + d2;
+  const float inv = __builtin_amdgcn_rcpf(b1 * b2);
+  o.ell = __builtin_fmaf(a1, d2, d1 * b2) * inv;
+  if constexpr (kTrain) {
+    // With S = A1 A2 inv, inv = 1/(B1 B2), and every term a multiple of D1,
+    // D2 or dmu (so all vanish when x = y):
+    //   dS/dmu_x' = 2 inv (mu_y T1 - mu_y' T2 + T3)
+    //   dS/dmu_y' = 2 inv (mu_x T1 - mu_x' T2 - T3)
+    //   dS/dP'    = 2 inv T2,      dS/dR = -S / B2 = -S B1 inv
+    // where T1 = A2 D1 / B1, T2 = A1 D2 / B2, T3 = S (B1 - B2) dmu.
+    // Maps (loss = mean of 1 - S over M entries, k = -(2/M) inv):
+    //   m0 = -(1/M) dS/dmu_x' = k (mu_y T1 - mu_y' T2 + T3)
+    //   m1 = -(1/M) dS/dmu_y' = k (mu_x T1 - mu_x' T2 - T3)
+    //   m2 = -(2/M) dS/dR     = -k S B1
+    //   m3 = -(1/M) dS/dP'    = k T2
+    const float s = a1 * a2 * inv;
+    const float ib1 = b2 * inv;
+    const float ib2 = b1 * inv;
+    const float t1 = a2 * d1 * ib1;
+    const float t2 = a1 * d2 * ib2;
+    const float t3 = s * (b1 - b2) * dm;
+    const float k = k_m2 * inv;
+    o.m[0] = k * __builtin_fmaf(muy, t1, __builtin_fmaf(-mys, t2, t3));
+    o.m[1] = k * __builtin_fmaf(mux, t1, __builtin_fmaf(-mxs, t2, -t3));
+    o.m[2] = -(k * s) * b1;
+    o.m[3] = k * t2;
+  }
+  return o;
+}
+
+template <int MODE, bool kVec>
+__device__ __forceinline__ void consume(const Params& p, int64_t plane, int i, int j,
+                                        const float (&o)[kQ][4], float dl, double& acc) {
+  if constexpr (MODE != kBwd) {
+    constexpr bool kTrain = (MODE == kFwdTrain);
+    float s4 = 0.0f;
+    float m[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const SsimOut r = ssim_point<kTrain>(o[0][t], o[1][t], o[2][t], o[3][t], p.k_m2);
+      const bool in = (j + t) < p.out_w;
+      s4 += in ? r.ell : 0.0f;
+      if constexpr (kTrain) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m[k][t] = in ? r.m[k] : 0.0f;
+      }
+    }
+    acc += (double)s4;
+    if constexpr (kTrain) {
+      // j is a multiple of 4 and the pitch rounds Wo up to one, so the whole
+      // group lies inside the padded row.
+      float* base = p.maps + plane * 4 * p.map_plane + (int64_t)i * p.map_pitch + j;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<float4*>(base + k * p.map_plane) =
+            make_float4(m[k][0], m[k][1], m[k][2], m[k][3]);
+    }
+  } else {
+    const int64_t pix = plane * p.img_plane + (int64_t)i * p.img_w + j;
+    float xv[4], yv[4];
+    if constexpr (kVec) {
+      const float4 a = *reinterpret_cast<const float4*>(p.x + pix);
+      const float4 b = *reinterpret_cast<const float4*>(p.y + pix);
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+      yv[0] = b.x; yv[1] = b.y; yv[2] = b.z; yv[3] = b.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool in = (j + t) < p.out_w;
+        xv[t] = in ? p.x[pix + t] : 0.0f;
+        yv[t] = in ? p.y[pix + t] : 0.0f;
+      }
+    }
+    float g1[4], g2[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // chain rule: d mu_x'/dx = B^T, d P'/dx = y' B^T, d R/dx = 2 (x - y) B^T
+      const float xs = xv[t] - kShift, ys = yv[t] - kShift, d = xv[t] - yv[t];
+      g1[t] = dl * __builtin_fmaf(d, o[2][t], __builtin_fmaf(ys, o[3][t], o[0][t]));
+      g2[t] = dl * __builtin_fmaf(-d, o[2][t], __builtin_fmaf(xs, o[3][t], o[1][t]));
+    }
+    if constexpr (kVec) {
+      if (p.gx) *reinterpret_cast<float4*>(p.gx + pix) = make_float4(g1[0], g1[1], g1[2], g1[3]);
+      if (p.gy) *reinterpret_cast<float4*>(p.gy + pix) = make_float4(g2[0], g2[1], g2[2], g2[3]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if ((j + t) < p.out_w) {
+          if (p.gx) p.gx[pix + t] = g1[t];
+          if (p.gy) p.gy[pix + t] = g2[t];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One batch of kRows rows: column pass into the ring and the LDS tile, then
+// the row pass and the consumer.  PH = batch index mod 3 fixes the ring slots
+// at compile time.
+
+template <int MODE, bool kVec, int PH>
+__device__ __forceinline__ void batch(const Params& p, float (&tile)[2][kQ][kRows][kTileW],
+                                      float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows],
+                                      const float* c0, const float* c1, bool col_ok, int r0,
+                                      int t, int nb, int buf, int64_t plane, int row0, int nrows,
+                                      int j0, float dl, double& acc) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+
+  Raw<MODE> cur[kRows];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) cur[m] = pre[m];
+  if (t + 1 < nb) {
+#pragma unroll
+    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, c0, c1, col_ok, r0 + 10 + 4 * (t + 1) + m, pre[m]);
+  }
+
+  // column pass
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    constexpr int kBase = 0;
+    const int base = 4 * PH + m;  // compile-time after unrolling
+    (void)kBase;
+    quantities<MODE>(cur[m], ring[(base + 10) % kRing]);
+    float cs[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) cs[q] = tap(0) * ring[base % kRing][q];
+#pragma unroll
+    for (int a = 1; a < 11; ++a)
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) cs[q] = __builtin_fmaf(tap(a), ring[(base + a) % kRing][q], cs[q]);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
+  }
+  __syncthreads();
+
+  // row pass: wave w -> batch row w; lane l -> outputs 4l .. 4l+3
+  const int ri = 4 * t + wave;
+  const int j = j0 + 4 * lane;
+  if (ri < nrows && lane < kRowLanes && j < p.out_w) {
+    float o[kQ][4];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const float* src = &tile[buf][q][wave][4 * lane];
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+        v[4 * k + 0] = f.x;
+        v[4 * k + 1] = f.y;
+        v[4 * k + 2] = f.z;
+        v[4 * k + 3] = f.w;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float s = tap(0) * v[u];
+#pragma unroll
+        for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), v[u + b], s);
+        o[q][u] = s;
+      }
+    }
+    consume<MODE, kVec>(p, plane, row0 + ri, j, o, dl, acc);
+  }
+}
+
+template <int MODE, bool kVec>
+__global__ __launch_bounds__(kThreads) void ssim_strip_kernel(const Params p) {
+  __shared__ float tile[2][kQ][kRows][kTileW];
+  __shared__ double red[kWaves];
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x;
+  const int G = gridDim.x;
+  // XCD-aware order: hardware hands consecutive workgroup ids to the 8 XCDs
+  // in turn; give each XCD one contiguous eighth of the work.
+  int lb = blockIdx.x;
+  if ((G & 7) == 0) lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int64_t u_begin = (int64_t)lb * p.units / G;
+  const int64_t u_end = (int64_t)(lb + 1) * p.units / G;
+
+  float dl = 0.0f;
+  if constexpr (MODE == kBwd) dl = *p.dloss;
+
+  double acc = 0.0;
+  int buf = 0;
+  const int64_t per_plane = (int64_t)p.strips * p.out_h;
+  for (int64_t u = u_begin; u < u_end;) {
+    const int64_t plane = u / per_plane;
+    const int64_t rem = u - plane * per_plane;
+    const int strip = (int)(rem / p.out_h);
+    const int row0 = (int)(rem - (int64_t)strip * p.out_h);
+    const int64_t left = u_end - u;
+    const int nrows = (int)((int64_t)(p.out_h - row0) < left ? (int64_t)(p.out_h - row0) : left);
+    u += nrows;
+
+    const int j0 = strip * kStripOut;
+    const int c = j0 - p.off + tid;  // this lane's input column
+    const bool col_ok = (c >= 0) && (c < p.in_w);
+    const int cc = col_ok ? c : 0;
+    const float* c0;
+    const float* c1 = nullptr;
+    if constexpr (MODE == kBwd) {
+      c0 = p.maps + plane * 4 * p.map_plane + cc;
+    } else {
+      c0 = p.x + plane * p.in_plane + cc;
+      c1 = p.y + plane * p.in_plane + cc;
+    }
+    const int r0 = row0 - p.off;  // input row held by ring slot 0
+    const int nb = (nrows + kRows - 1) / kRows;
+
+    float ring[kRing][kQ];
+    Raw<MODE> warm[10];
+    Raw<MODE> pre[kRows];
+#pragma unroll
+    for (int k = 0; k < 10; ++k) load_row<MODE>(p, c0, c1, col_ok, r0 + k, warm[k]);
+#pragma unroll
+    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, c0, c1, col_ok, r0 + 10 + m, pre[m]);
+#pragma unroll
+    for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], ring[k]);
+
+    for (int t = 0;;) {
+      if (t >= nb) break;
+      batch<MODE, kVec, 0>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      buf ^= 1;
+      if (++t >= nb) break;
+      batch<MODE, kVec, 1>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      buf ^= 1;
+      if (++t >= nb) break;
+      batch<MODE, kVec, 2>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      buf ^= 1;
+      ++t;
+    }
+  }
+
+  if constexpr (MODE != kBwd) {
+    // workgroup sum of the SSIM map, then the last workgroup finishes the mean
+    const int wave = tid / kWave, lane = tid % kWave;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (lane == 0) red[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      double bs = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) bs += red[w];
+      __hip_atomic_store(&p.ws->partial[blockIdx.x], bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned prev =
+          __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = (prev == (unsigned)(G - 1));
+    }
+    __syncthreads();
+    if (is_last && wave == 0) {
+      double s = 0.0;
+      for (int k = lane; k < G; k += kWave)
+        s += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+      if (lane == 0) {
+        *p.loss = (float)(s * p.inv_m);
+        __hip_atomic_store(&p.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+
+struct DeviceInfo {
+  bool ready = false;
+  int status = SSIM_OK;
+  int cus = 0;
+  int occ[4] = {0, 0, 0, 0};  // resident workgroups per CU: fwd-infer, fwd-train, bwd-vec, bwd-scalar
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+int device_info(const DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSIM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSIM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SSIM_ERR_HIP;
+    if (prop.warpSize != kWave || strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      d.status = SSIM_ERR_DEVICE;
+    } else {
+      d.cus = prop.multiProcessorCount;
+      const void* ks[4] = {(const void*)ssim_strip_kernel<kFwdInfer, false>,
+                           (const void*)ssim_strip_kernel<kFwdTrain, false>,
+                           (const void*)ssim_strip_kernel<kBwd, true>,
+                           (const void*)ssim_strip_kernel<kBwd, false>};
+      for (int k = 0; k < 4; ++k) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ks[k], kThreads, 0) != hipSuccess)
+          return SSIM_ERR_HIP;
+        d.occ[k] = n > 0 ? n : 1;
+      }
+      d.status = SSIM_OK;
+    }
+    d.ready = true;
+  }
+  *out = &d;
+  return d.status;
+}
+
+int64_t roundup4(int64_t v) { return (v + 3) & ~(int64_t)3; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+struct Shape {
+  int64_t N, C, H, W, Ho, Wo, pitch, planes;
+  size_t img_bytes, map_bytes;
+};
+
+int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, Shape* s) {
+  if (padding != SSIM_PAD_VALID && padding != SSIM_PAD_SAME) return SSIM_ERR_PADDING;
+  if (N <= 0 || C <= 0 || H <= 0 || W <= 0) return SSIM_ERR_SHAPE;
+  const int64_t Ho = padding == SSIM_PAD_VALID ? H - 10 : H;
+  const int64_t Wo = padding == SSIM_PAD_VALID ? W - 10 : W;
+  if (Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 31;
+  if (H > lim / W) return SSIM_ERR_OVERFLOW;
+  const int64_t pitch = roundup4(Wo);
+  if (Ho > (lim - 1) / pitch || H * W >= lim || Ho * pitch >= lim) return SSIM_ERR_OVERFLOW;
+  if (N > (int64_t)1 << 40 || C > ((int64_t)1 << 40) / N) return SSIM_ERR_OVERFLOW;
+  const int64_t planes = N * C;
+  // bytes must fit comfortably in 64 bits
+  if (planes > ((int64_t)1 << 58) / (H * W) || planes > ((int64_t)1 << 56) / (Ho * pitch))
+    return SSIM_ERR_OVERFLOW;
+  s->N = N; s->C = C; s->H = H; s->W = W; s->Ho = Ho; s->Wo = Wo; s->pitch = pitch;
+  s->planes = planes;
+  s->img_bytes = (size_t)(planes * H * W) * sizeof(float);
+  s->map_bytes = (size_t)(planes * Ho * pitch) * 4 * sizeof(float);
+  return SSIM_OK;
+}
+
+int grid_for(const DeviceInfo* d, int which, int64_t units) {
+  int64_t g = (units + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
+  const int64_t resident = (int64_t)d->cus * d->occ[which];
+  if (g > resident) g = resident;
+  if (g > kMaxBlocks) g = kMaxBlocks;
+  if (g >= 8) g &= ~(int64_t)7;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane, int out_h,
+                   int out_w, int off, int64_t planes) {
+  p.in_h = in_h;
+  p.in_w = in_w;
+  p.in_pitch = in_pitch;
+  p.in_plane = in_plane;
+  p.out_h = out_h;
+  p.out_w = out_w;
+  p.off = off;
+  p.strips = (out_w + kStripOut - 1) / kStripOut;
+  p.units = planes * p.strips * (int64_t)out_h;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int ssim_abi_version(void) { return SSIM_ABI_VERSION; }
+
+const char* ssim_strerror(int code) {
+  switch (code) {
+    case SSIM_OK: return "success";
+    case SSIM_ERR_NULL: return "a required pointer is NULL";
+    case SSIM_ERR_SHAPE: return "bad shape: N, C, H, W must be positive and valid padding needs H, W >= 11";
+    case SSIM_ERR_PADDING: return "padding must be SSIM_PAD_VALID (0) or SSIM_PAD_SAME (1)";
+    case SSIM_ERR_OVERFLOW: return "a plane holds 2^31 or more elements, or a size overflows";
+    case SSIM_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case SSIM_ERR_HIP: return "a HIP runtime call failed";
+    case SSIM_ERR_DEVICE: return "the current device is not a wave64 gfx950 GPU";
+    default: return "unknown error code";
+  }
+}
+
+void ssim_taps(float out[11]) {
+  for (int k = 0; k < 11; ++k) out[k] = tap(k);
+}
+
+int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo) {
+  if (!Ho || !Wo) return SSIM_ERR_NULL;
+  Shape s;
+  const int rc = check_shape(1, 1, H, W, padding, &s);
+  if (rc != SSIM_OK) return rc;
+  *Ho = s.Ho;
+  *Wo = s.Wo;
+  return SSIM_OK;
+}
+
+size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding) {
+  Shape s;
+  if (check_shape(N, C, H, W, padding, &s) != SSIM_OK) return 0;
+  return s.map_bytes;
+}
+
+size_t ssim_workspace_bytes(void) { return sizeof(Workspace); }
+
+int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int64_t H,
+                 int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
+                 void* stream) {
+  if (!img1 || !img2 || !loss || !workspace) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, &s);
+  if (rc != SSIM_OK) return rc;
+  if (saved_maps && ((uintptr_t)saved_maps & 15u)) return SSIM_ERR_SHAPE;
+  const size_t wsb = sizeof(Workspace);
+  const void* outs[3] = {loss, saved_maps, workspace};
+  const size_t outb[3] = {sizeof(float), saved_maps ? s.map_bytes : 0, wsb};
+  for (int k = 0; k < 3; ++k) {
+    if (overlaps(outs[k], outb[k], img1, s.img_bytes) || overlaps(outs[k], outb[k], img2, s.img_bytes))
+      return SSIM_ERR_ALIAS;
+    for (int l = k + 1; l < 3; ++l)
+      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
+  }
+
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  const int off = padding == SSIM_PAD_VALID ? 0 : 5;
+  fill_geometry(p, (int)s.H, (int)s.W, (int)s.W, s.H * s.W, (int)s.Ho, (int)s.Wo, off, s.planes);
+  p.x = img1;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.maps = saved_maps;
+  p.map_pitch = (int)s.pitch;
+  p.map_plane = s.Ho * s.pitch;
+  const double M = (double)s.planes * (double)s.Ho * (double)s.Wo;
+  p.k_m2 = (float)(-2.0 / M);
+  p.inv_m = 1.0 / M;
+  p.loss = loss;
+  p.ws = static_cast<Workspace*>(workspace);
+
+  const int which = saved_maps ? 1 : 0;
+  const int G = grid_for(d, which, p.units);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (saved_maps)
+    hipLaunchKernelGGL((ssim_strip_kernel<kFwdTrain, false>), dim3(G), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((ssim_strip_kernel<kFwdInfer, false>), dim3(G), dim3(kThreads), 0, st, p);
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
+}
+
+int ssim_backward(const float* dloss, const float* img1, const float* img2, int64_t N,
+                  int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
+                  float* grad_img1, float* grad_img2, void* stream) {
+  if (!dloss || !img1 || !img2 || !saved_maps) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, &s);
+  if (rc != SSIM_OK) return rc;
+  if ((uintptr_t)saved_maps & 15u) return SSIM_ERR_SHAPE;
+  const void* ins[4] = {dloss, img1, img2, saved_maps};
+  const size_t inb[4] = {sizeof(float), s.img_bytes, s.img_bytes, s.map_bytes};
+  float* outs[2] = {grad_img1, grad_img2};
+  for (int k = 0; k < 2; ++k)
+    for (int l = 0; l < 4; ++l)
+      if (overlaps(outs[k], s.img_bytes, ins[l], inb[l])) return SSIM_ERR_ALIAS;
+  if (overlaps(grad_img1, s.img_bytes, grad_img2, s.img_bytes)) return SSIM_ERR_ALIAS;
+  if (!grad_img1 && !grad_img2) return SSIM_OK;
+
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  const int off = padding == SSIM_PAD_VALID ? 10 : 5;
+  fill_geometry(p, (int)s.Ho, (int)s.Wo, (int)s.pitch, s.Ho * s.pitch * 4, (int)s.H, (int)s.W,
+                off, s.planes);
+  p.x = img1;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.maps = const_cast<float*>(saved_maps);
+  p.map_pitch = (int)s.pitch;
+  p.map_plane = s.Ho * s.pitch;
+  p.dloss = dloss;
+  p.gx = grad_img1;
+  p.gy = grad_img2;
+
+  const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % 16 == 0) && ((uintptr_t)img2 % 16 == 0) &&
+                   ((uintptr_t)grad_img1 % 16 == 0) && ((uintptr_t)grad_img2 % 16 == 0);
+  const int G = grid_for(d, vec ? 2 : 3, p.units);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (vec)
+    hipLaunchKernelGGL((ssim_strip_kernel<kBwd, true>), dim3(G), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((ssim_strip_kernel<kBwd, false>), dim3(G), dim3(kThreads), 0, st, p);
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol the header declares, and rejects bad arguments with the
+documented codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import ssim_loss_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssim_loss_amd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssim_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["ssim_forward", "ssim_backward", "ssim_saved_maps_bytes", "ssim_workspace_bytes",
+              "ssim_strerror", "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(S.build.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strerror():
+    assert S.ssim_abi_version() == 1
+    for code in range(0, -8, -1):
+        assert S.ssim_strerror(code)
+    assert "unknown" in S.ssim_strerror(-99)
+
+
+def test_kernel_taps_are_the_oracle_taps_rounded_once():
+    g = np.array(S.ssim_taps(), np.float32)
+    np.testing.assert_array_equal(g, oracle.taps().astype(np.float32))
+    np.testing.assert_array_equal(g, g[::-1])
+
+
+@pytest.mark.parametrize("H,W,padding", [(11, 11, "valid"), (64, 37, "valid"), (1, 1, "same"),
+                                         (1080, 1920, "same"), (2160, 3840, "valid")])
+def test_map_shape_matches_oracle(H, W, padding):
+    assert S.ssim_map_shape(H, W, padding) == oracle.out_shape(H, W, padding)
+
+
+def test_saved_maps_bytes():
+    # four fp32 maps per plane, row pitch = Wo rounded up to 4
+    assert S.ssim_saved_maps_bytes(1, 3, 1080, 1920, "valid") == 16 * 3 * 1070 * 1912
+    assert S.ssim_saved_maps_bytes(1, 3, 1080, 1920, "same") == 16 * 3 * 1080 * 1920
+    assert S.ssim_saved_maps_bytes(8, 3, 2160, 3840, "valid") == 16 * 24 * 2150 * 3832
+    assert S.ssim_saved_maps_bytes(1, 1, 10, 30, "valid") == 0
+    assert S.ssim_saved_maps_bytes(1, 1, 30, 30, 7) == 0
+    assert S.ssim_workspace_bytes() >= 8 * 1024
+
+
+def _fwd(lib, img1=0x1000, img2=0x100000, N=1, C=1, H=64, W=64, padding=0, loss=0x200000,
+         maps=0x300000, ws=0x900000):
+    return lib.ssim_forward(img1, img2, N, C, H, W, padding, loss, maps, ws, None)
+
+
+def _bwd(lib, dloss=0x1000, img1=0x10000, img2=0x100000, N=1, C=1, H=64, W=64, padding=0,
+         maps=0x300000, g1=0x900000, g2=0xA00000):
+    return lib.ssim_backward(dloss, img1, img2, N, C, H, W, padding, maps, g1, g2, None)
+
+
+def test_forward_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    assert _fwd(lib, img1=None) == -1
+    assert _fwd(lib, loss=None) == -1
+    assert _fwd(lib, ws=None) == -1
+    assert _fwd(lib, padding=2) == -3
+    assert _fwd(lib, N=0) == -2
+    assert _fwd(lib, C=-1) == -2
+    assert _fwd(lib, H=10) == -2          # valid needs H >= 11
+    assert _fwd(lib, W=10) == -2
+    assert _fwd(lib, H=1 << 16, W=1 << 16) == -4   # a plane of 2^32 elements
+    assert _fwd(lib, maps=0x300004) == -2          # saved maps must be 16-byte aligned
+    assert _fwd(lib, loss=0x1000 + 64) == -5       # loss inside img1
+    assert _fwd(lib, maps=0x100000 + 4096) == -5   # maps overlap img2
+    assert _fwd(lib, ws=0x300000 + 1024) == -5     # workspace overlaps maps
+
+
+def test_backward_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    assert _bwd(lib, dloss=None) == -1
+    assert _bwd(lib, maps=None) == -1
+    assert _bwd(lib, img2=None) == -1
+    assert _bwd(lib, padding=-1) == -3
+    assert _bwd(lib, H=5, padding=0) == -2
+    assert _bwd(lib, g1=0x10000 + 128) == -5          # grad overlaps img1
+    assert _bwd(lib, g2=0x900000 + 8) == -5           # grads overlap each other
+    assert _bwd(lib, g1=0x300000 + 16) == -5          # grad overlaps the maps
+    assert _bwd(lib, g1=None, g2=None) == 0           # nothing to do: no launch
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(TypeError):
+        S.ssim_loss(x, x)
+    with pytest.raises(TypeError):
+        S.ssim_loss(x.double(), x.double())

@@ -1,0 +1,215 @@
+"""Edge, ragged, random and degenerate cases of the HIP path against the
+oracle (and against closed forms where the oracle's answer is known)."""
+import numpy as np
+import pytest
+
+import oracle
+from ssim_loss_amd.inputs import make_pair
+
+from gpu_util import GRAD_RTOL, check_grad, check_loss, gpu_run, say
+
+pytestmark = pytest.mark.gpu
+
+# sizes around the window (11), the strip (244 outputs / 256 inputs), the
+# 4-wide output groups and the 4-row batches
+EDGE_HW = [(11, 11), (12, 13), (13, 12), (20, 21), (21, 20), (31, 64), (63, 65), (64, 64),
+           (65, 63), (127, 129), (254, 11), (11, 254), (255, 256), (256, 257), (257, 255),
+           (100, 498), (60, 499), (33, 500), (14, 1001), (1001, 14)]
+
+
+@pytest.mark.parametrize("padding", ["valid", "same"])
+@pytest.mark.parametrize("hw", EDGE_HW, ids=lambda hw: f"{hw[0]}x{hw[1]}")
+def test_edge_shapes(hw, padding):
+    H, W = hw
+    say(f"[edge] {H}x{W} {padding}")
+    x, y = make_pair((1, 2, H, W), "uniform", 0.1, seed=H * 1000 + W)
+    gl, g1, g2 = gpu_run(x, y, padding, dloss=1.7)
+    ol, o1, o2 = oracle.ssim_loss(x, y, padding, dloss=1.7)
+    check_loss(gl, ol)
+    check_grad(g1, o1, "grad_img1")
+    check_grad(g2, o2, "grad_img2")
+
+
+@pytest.mark.parametrize("H,W", [(1, 1), (1, 7), (5, 1), (3, 3), (10, 10)])
+def test_same_padding_images_smaller_than_window(H, W):
+    say(f"[edge] tiny same {H}x{W}")
+    x, y = make_pair((2, 1, H, W), "uniform", 0.2, seed=H + 7 * W)
+    gl, g1, g2 = gpu_run(x, y, "same")
+    ol, o1, o2 = oracle.ssim_loss(x, y, "same")
+    check_loss(gl, ol)
+    check_grad(g1, o1, "grad_img1")
+    check_grad(g2, o2, "grad_img2")
+
+
+def _random_cases(n=40):
+    rng = np.random.default_rng(2024)
+    cases = []
+    for k in range(n):
+        N = int(rng.integers(1, 4))
+        C = int(rng.integers(1, 5))
+        H = int(rng.integers(11, 300))
+        W = int(rng.integers(11, 600))
+        cases.append((k, N, C, H, W, "valid" if rng.random() < 0.5 else "same",
+                      ["uniform", "field"][int(rng.integers(2))], float(rng.uniform(0.01, 0.3))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"r{c[0]}")
+def test_random_shapes(case):
+    k, N, C, H, W, padding, kind, noise = case
+    say(f"[random] {k}: {N}x{C}x{H}x{W} {padding} {kind} noise {noise:.3f}")
+    x, y = make_pair((N, C, H, W), kind, noise, seed=100 + k)
+    dloss = [1.0, -0.5, 3.0][k % 3]
+    gl, g1, g2 = gpu_run(x, y, padding, dloss=dloss)
+    ol, o1, o2 = oracle.ssim_loss(x, y, padding, dloss=dloss)
+    check_loss(gl, ol)
+    check_grad(g1, o1, "grad_img1")
+    check_grad(g2, o2, "grad_img2")
+
+
+@pytest.mark.parametrize("padding", ["valid", "same"])
+def test_identical_images_give_exact_zero(padding):
+    """x = y: SSIM is exactly 1 and both gradients vanish (oracle pins).  The
+    kernels form 1 - S and every partial from x - y, mu_x - mu_y and
+    var(x - y), which are exactly zero here, so the fp32 result is exact."""
+    say(f"[stability] identical {padding}")
+    x, _ = make_pair((1, 3, 96, 80), "field", 0.05, seed=3)
+    gl, g1, g2 = gpu_run(x, x, padding)
+    assert gl == 0.0
+    assert not g1.any() and not g2.any()
+    for v in (0.0, 1.0):
+        c = np.full((2, 1, 32, 32), v, np.float32)
+        gl, g1, g2 = gpu_run(c, c, padding)
+        assert gl == 0.0 and not g1.any() and not g2.any()
+
+
+def _constant_bound(a, b):
+    """fp32 error model for constant images.  Their variances vanish, so
+    B2 = C2 + (rounding residue of R - dmu^2 and of P' - mu_x' mu_y'), a few
+    ulps of (a - b)^2 and |(a - 1/2)(b - 1/2)|; S, 1 - S and every partial
+    then carry that residue relative to C2 = 9e-4."""
+    return 64 * 2.0 ** -24 * ((a - b) ** 2 + 2 * abs((a - 0.5) * (b - 0.5))) / 9e-4
+
+
+@pytest.mark.parametrize("padding", ["valid", "same"])
+@pytest.mark.parametrize("a,b", [(0.25, 0.75), (0.0, 1.0), (0.9, 0.1), (0.5, 0.5)])
+def test_constant_images(a, b, padding):
+    """Constant images against the oracle, within the fp32 error model above;
+    in valid padding also against S = (2ab + C1)/(a^2 + b^2 + C1)."""
+    say(f"[stability] constant {a} {b} {padding}")
+    x = np.full((1, 2, 40, 50), a, np.float32)
+    y = np.full((1, 2, 40, 50), b, np.float32)
+    bound = _constant_bound(a, b)
+    gl, g1, g2 = gpu_run(x, y, padding)
+    if a == b:  # identical images: exactly zero (the oracle shows fp64 noise here)
+        assert gl == 0.0 and not g1.any() and not g2.any()
+        return
+    ol, o1, o2 = oracle.ssim_loss(x, y, padding)
+    assert abs(gl - ol) <= max(bound, 1e-5 * abs(ol))
+    if padding == "valid":
+        S = (2 * a * b + 1e-4) / (a * a + b * b + 1e-4)
+        assert abs((1 - gl) - S) <= max(bound, 1e-5 * abs(1 - S))
+    for g, og in ((g1, o1), (g2, o2)):
+        scale = float(np.abs(og).max())
+        err = float(np.abs(g.astype(np.float64) - og).max())
+        assert err <= max(bound, GRAD_RTOL) * scale
+
+
+def test_zero_against_one():
+    say("[stability] zeros vs ones")
+    z = np.zeros((1, 1, 32, 32), np.float32)
+    o = np.ones((1, 1, 32, 32), np.float32)
+    gl, g1, g2 = gpu_run(z, o, "same")
+    ol, o1, o2 = oracle.ssim_loss(z, o, "same")
+    bound = _constant_bound(0.0, 1.0)
+    assert abs(gl - ol) <= max(bound, 1e-5 * abs(ol))
+    for g, og in ((g1, o1), (g2, o2)):
+        assert float(np.abs(g - og).max()) <= max(bound, GRAD_RTOL) * float(np.abs(og).max())
+
+
+def test_nullable_gradients_and_dloss_scaling():
+    say("[api] grad_img1 / grad_img2 = NULL, dloss scaling")
+    x, y = make_pair((2, 3, 70, 90), "uniform", 0.1, seed=11)
+    _, a1, a2 = gpu_run(x, y, "valid", dloss=1.0)
+    _, b1, b2 = gpu_run(x, y, "valid", dloss=-2.5)
+    np.testing.assert_allclose(b1, -2.5 * a1, rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(b2, -2.5 * a2, rtol=1e-6, atol=1e-12)
+    _, c1, c2 = gpu_run(x, y, "valid", grad2=False)
+    assert c2 is None
+    np.testing.assert_array_equal(c1, a1)
+    _, d1, d2 = gpu_run(x, y, "valid", grad1=False)
+    assert d1 is None
+    np.testing.assert_array_equal(d2, a2)
+
+
+def test_inference_forward_matches_training_forward():
+    say("[api] saved_maps = NULL")
+    x, y = make_pair((1, 3, 200, 300), "field", 0.05, seed=12)
+    for padding in ("valid", "same"):
+        lt, _, _ = gpu_run(x, y, padding)
+        li, _, _ = gpu_run(x, y, padding, train=False)
+        assert abs(lt - li) <= 1e-7 * abs(lt)
+
+
+def test_deterministic_run_to_run():
+    say("[api] determinism")
+    x, y = make_pair((2, 3, 150, 260), "uniform", 0.05, seed=13)
+    r = [gpu_run(x, y, "valid") for _ in range(3)]
+    for k in (1, 2):
+        assert r[k][0] == r[0][0]
+        np.testing.assert_array_equal(r[k][1], r[0][1])
+        np.testing.assert_array_equal(r[k][2], r[0][2])
+
+
+def test_autograd_functions():
+    import torch
+
+    import ssim_loss_amd as S
+
+    say("[api] autograd")
+    x, y = make_pair((2, 3, 64, 96), "uniform", 0.1, seed=14)
+    dev = torch.device("cuda")
+    t1 = torch.from_numpy(x).to(dev).requires_grad_(True)
+    t2 = torch.from_numpy(y).to(dev)
+    loss = S.ssim_loss(t1, t2, "valid")
+    (0.5 * loss).backward()
+    ol, o1, _ = oracle.ssim_loss(x, y, "valid", dloss=0.5)
+    check_loss(float(loss.item()), ol)
+    check_grad(t1.grad.cpu().numpy(), o1, "grad_img1")
+    assert t2.grad is None
+    # fused_ssim: mean SSIM, default padding "same"
+    t1.grad = None
+    s = S.fused_ssim(t1, t2)
+    s.backward()
+    sl, s1, _ = oracle.ssim_loss(x, y, "same", dloss=-1.0)
+    assert abs(float(s.item()) - (1 - sl)) <= 1e-5 * abs(sl)
+    check_grad(t1.grad.cpu().numpy(), s1, "fused_ssim grad")
+    with torch.no_grad():
+        v = S.fused_ssim(t1, t2, train=False)
+    assert abs(float(v.item()) - (1 - sl)) <= 1e-5 * abs(sl)
+
+
+def test_workspace_reuse_across_shapes():
+    """The completion counter is reset by every forward, so one workspace
+    serves calls of any size in sequence."""
+    say("[api] workspace reuse")
+    for k, shape in enumerate([(1, 1, 300, 300), (1, 1, 20, 20), (3, 2, 120, 80), (1, 1, 20, 20)]):
+        x, y = make_pair(shape, "uniform", 0.1, seed=20 + k)
+        gl, _, _ = gpu_run(x, y, "same", train=False)
+        ol, _, _ = oracle.ssim_loss(x, y, "same", grads=False)
+        check_loss(gl, ol)
+
+
+def test_rejects_bad_inputs_on_gpu():
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    a = torch.rand(1, 1, 32, 32, device=dev)
+    with pytest.raises(ValueError):
+        S.ssim_loss(a, torch.rand(1, 1, 32, 31, device=dev))
+    with pytest.raises(ValueError):
+        S.ssim_loss(a.transpose(2, 3), a)
+    with pytest.raises(S.SsimError):
+        S.ssim_loss(torch.rand(1, 1, 8, 32, device=dev), torch.rand(1, 1, 8, 32, device=dev), "valid")
