@@ -52,8 +52,8 @@ enum {
   SSIM_ERR_NULL = -1,     /* a required pointer is NULL */
   SSIM_ERR_SHAPE = -2,    /* N, C, H or W <= 0, or valid padding with H < 11 or W < 11 */
   SSIM_ERR_PADDING = -3,  /* padding is neither SSIM_PAD_VALID nor SSIM_PAD_SAME */
-  SSIM_ERR_OVERFLOW = -4, /* one plane (or one map plane) holds 2^31 or more elements,
-                             or a buffer size overflows size_t */
+  SSIM_ERR_OVERFLOW = -4, /* a plane (image or map) holds more than 2^27 elements, a row
+                             more than 2^20, or a buffer size overflows */
   SSIM_ERR_ALIAS = -5,    /* an output buffer overlaps an input or another output */
   SSIM_ERR_HIP = -6,      /* a HIP runtime call failed (launch, device query) */
   SSIM_ERR_DEVICE = -7    /* the current device is not a wave64 gfx9 GPU */
@@ -94,7 +94,9 @@ size_t ssim_workspace_bytes(void);
  * of SSIM, M = N*C*Ho*Wo, and writes it as one fp32 to `loss` (device).
  *
  *   img1, img2  : fp32 NCHW device images (inputs, not modified)
- *   N, C, H, W  : shape; each plane must hold fewer than 2^31 elements
+ *   N, C, H, W  : shape; a plane holds at most 2^27 elements (and its
+ *                 map, Ho rows of roundup(Wo, 4), as well), a row at most
+ *                 2^20; N*C is unbounded
  *   padding     : SSIM_PAD_VALID or SSIM_PAD_SAME
  *   loss        : device fp32 scalar (output)
  *   saved_maps  : NULL for inference (no gradient will be taken), else a

@@ -160,32 +160,66 @@ struct Params {
 };
 
 // ---------------------------------------------------------------------------
-// Column loads and the quantities they feed
+// Memory access through buffer descriptors
+//
+// Every global load and store goes through a raw buffer descriptor covering
+// exactly one plane.  The hardware range-checks each access against the
+// descriptor's size: an out-of-range load returns 0 and an out-of-range store
+// is dropped.  Zero padding, the ragged right edge, rows above or below a
+// plane and idle lanes are all expressed as out-of-range offsets (a negative
+// row offset wraps to a large unsigned value; an invalid column uses the
+// 2^31 marker), so the hot loop has no branches around memory operations and
+// the compiler can keep loads in flight across the stores of a batch.
+// Planes are limited to 2^27 elements so that every valid byte offset, and
+// every marked one, stays on its side of 2^31.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr unsigned kOob = 0x80000000u;         // offset that is out of range for every plane
+constexpr int kRsrcFlags = 0x00020000;          // gfx9 dword3: 32-bit data format, raw access
+
+__device__ __forceinline__ rsrc_t make_rsrc(const float* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+__device__ __forceinline__ float ld1(rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float4 ld4(rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void st1(rsrc_t r, unsigned off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void st4(rsrc_t r, unsigned off, float4 v) {
+  using u4 = unsigned __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Per-segment context: one (plane, strip) and a run of its output rows
 
 template <int MODE>
-struct Raw;
-template <>
-struct Raw<kFwdInfer> { float v[2]; };
-template <>
-struct Raw<kFwdTrain> { float v[2]; };
-template <>
-struct Raw<kBwd> { float v[4]; };
+struct Seg {
+  static constexpr int kIn = (MODE == kBwd) ? 4 : 2;
+  rsrc_t in[kIn];       // fwd: x, y planes; bwd: the 4 map planes
+  rsrc_t img[2];        // bwd: x, y planes (chain rule)
+  rsrc_t out[4];        // fwd-train: the 4 map planes; bwd: grad_x, grad_y planes
+  unsigned colbyte;     // this lane's input column in bytes, or kOob
+  unsigned in_row;      // input row pitch, bytes
+  unsigned out_row;     // output row pitch, bytes
+  int r0;               // input row held by ring slot 0 (first output row - off)
+  int row0, nrows;      // output rows [row0, row0 + nrows)
+  int j0;               // first output column of the strip
+};
 
-// Pixel (row r) of this lane's column; zero outside the input extent.
 template <int MODE>
-__device__ __forceinline__ void load_row(const Params& p, const float* __restrict__ c0,
-                                         const float* __restrict__ c1, bool col_ok, int r,
-                                         Raw<MODE>& out) {
-  const bool ok = col_ok && (unsigned)r < (unsigned)p.in_h;
-  if constexpr (MODE == kBwd) {
-    const int64_t o = (int64_t)r * p.in_pitch;
+struct Raw { float v[Seg<MODE>::kIn]; };
+
+// This lane's input pixel(s) in input row r; 0 outside the input extent.
+template <int MODE>
+__device__ __forceinline__ void load_row(const Seg<MODE>& s, int r, Raw<MODE>& out) {
+  const unsigned off = s.colbyte + (unsigned)r * s.in_row;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) out.v[k] = ok ? c0[o + k * p.map_plane] : 0.0f;
-  } else {
-    const int o = r * p.in_pitch;
-    out.v[0] = ok ? c0[o] : 0.0f;
-    out.v[1] = ok ? c1[o] : 0.0f;
-  }
+  for (int k = 0; k < Seg<MODE>::kIn; ++k) out.v[k] = ld1(s.in[k], off);
 }
 
 // Quantities blurred by the forward: x', y', (x - y)^2 and x' y' with
@@ -257,9 +291,47 @@ __device__ __forceinline__ SsimOut ssim_point(float mxs, float mys, float rr, fl
   return o;
 }
 
+// Where this lane's output group lives: byte offset of its first output in
+// the output planes, or kOob when the group is not real (row outside the
+// segment, lane outside the strip, first column outside the output extent).
+// The images read by the backward's chain rule are loaded here, at the start
+// of a batch, so that their latency hides behind the batch's blur work.
 template <int MODE, bool kVec>
-__device__ __forceinline__ void consume(const Params& p, int64_t plane, int i, int j,
-                                        const float (&o)[kQ][4], float dl, double& acc) {
+struct Group {
+  bool ok;
+  int j;
+  unsigned base;
+  unsigned off[4];  // scalar path: per-output offsets
+  float xv[4], yv[4];
+};
+
+template <int MODE, bool kVec>
+__device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s, int ri, int lane,
+                                            Group<MODE, kVec>& g) {
+  g.j = s.j0 + 4 * lane;
+  g.ok = (ri < s.nrows) && (lane < kRowLanes) && (g.j < p.out_w);
+  g.base = g.ok ? (unsigned)(s.row0 + ri) * s.out_row + (unsigned)g.j * 4u : kOob;
+  if constexpr (MODE == kBwd) {
+    if constexpr (kVec) {
+      const float4 a = ld4(s.img[0], g.base);
+      const float4 b = ld4(s.img[1], g.base);
+      g.xv[0] = a.x; g.xv[1] = a.y; g.xv[2] = a.z; g.xv[3] = a.w;
+      g.yv[0] = b.x; g.yv[1] = b.y; g.yv[2] = b.z; g.yv[3] = b.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        g.off[t] = (g.ok && (g.j + t) < p.out_w) ? g.base + 4u * t : kOob;
+        g.xv[t] = ld1(s.img[0], g.off[t]);
+        g.yv[t] = ld1(s.img[1], g.off[t]);
+      }
+    }
+  }
+}
+
+template <int MODE, bool kVec>
+__device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
+                                        const Group<MODE, kVec>& g, const float (&o)[kQ][4],
+                                        float dl, double& acc) {
   if constexpr (MODE != kBwd) {
     constexpr bool kTrain = (MODE == kFwdTrain);
     float s4 = 0.0f;
@@ -267,57 +339,39 @@ __device__ __forceinline__ void consume(const Params& p, int64_t plane, int i, i
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const SsimOut r = ssim_point<kTrain>(o[0][t], o[1][t], o[2][t], o[3][t], p.k_m2);
-      const bool in = (j + t) < p.out_w;
-      s4 += in ? r.ell : 0.0f;
+      s4 += (g.ok && (g.j + t) < p.out_w) ? r.ell : 0.0f;
       if constexpr (kTrain) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m[k][t] = in ? r.m[k] : 0.0f;
+        for (int k = 0; k < 4; ++k) m[k][t] = r.m[k];
       }
     }
     acc += (double)s4;
     if constexpr (kTrain) {
       // j is a multiple of 4 and the pitch rounds Wo up to one, so the whole
-      // group lies inside the padded row.
-      float* base = p.maps + plane * 4 * p.map_plane + (int64_t)i * p.map_pitch + j;
+      // group lies inside the padded row; entries past Wo land in the pitch
+      // padding, which nothing reads.
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<float4*>(base + k * p.map_plane) =
-            make_float4(m[k][0], m[k][1], m[k][2], m[k][3]);
+      for (int k = 0; k < 4; ++k) st4(s.out[k], g.base, make_float4(m[k][0], m[k][1], m[k][2], m[k][3]));
     }
   } else {
-    const int64_t pix = plane * p.img_plane + (int64_t)i * p.img_w + j;
-    float xv[4], yv[4];
-    if constexpr (kVec) {
-      const float4 a = *reinterpret_cast<const float4*>(p.x + pix);
-      const float4 b = *reinterpret_cast<const float4*>(p.y + pix);
-      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-      yv[0] = b.x; yv[1] = b.y; yv[2] = b.z; yv[3] = b.w;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool in = (j + t) < p.out_w;
-        xv[t] = in ? p.x[pix + t] : 0.0f;
-        yv[t] = in ? p.y[pix + t] : 0.0f;
-      }
-    }
     float g1[4], g2[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       // chain rule: d mu_x'/dx = B^T, d P'/dx = y' B^T, d R/dx = 2 (x - y) B^T
-      const float xs = xv[t] - kShift, ys = yv[t] - kShift, d = xv[t] - yv[t];
+      const float xs = g.xv[t] - kShift, ys = g.yv[t] - kShift, d = g.xv[t] - g.yv[t];
       g1[t] = dl * __builtin_fmaf(d, o[2][t], __builtin_fmaf(ys, o[3][t], o[0][t]));
       g2[t] = dl * __builtin_fmaf(-d, o[2][t], __builtin_fmaf(xs, o[3][t], o[1][t]));
     }
+    // a gradient the caller does not want has a zero-size descriptor: its
+    // stores are dropped without a branch
     if constexpr (kVec) {
-      if (p.gx) *reinterpret_cast<float4*>(p.gx + pix) = make_float4(g1[0], g1[1], g1[2], g1[3]);
-      if (p.gy) *reinterpret_cast<float4*>(p.gy + pix) = make_float4(g2[0], g2[1], g2[2], g2[3]);
+      st4(s.out[0], g.base, make_float4(g1[0], g1[1], g1[2], g1[3]));
+      st4(s.out[1], g.base, make_float4(g2[0], g2[1], g2[2], g2[3]));
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if ((j + t) < p.out_w) {
-          if (p.gx) p.gx[pix + t] = g1[t];
-          if (p.gy) p.gy[pix + t] = g2[t];
-        }
+        st1(s.out[0], g.off[t], g1[t]);
+        st1(s.out[1], g.off[t], g2[t]);
       }
     }
   }
@@ -329,29 +383,29 @@ __device__ __forceinline__ void consume(const Params& p, int64_t plane, int i, i
 // at compile time.
 
 template <int MODE, bool kVec, int PH>
-__device__ __forceinline__ void batch(const Params& p, float (&tile)[2][kQ][kRows][kTileW],
-                                      float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows],
-                                      const float* c0, const float* c1, bool col_ok, int r0,
-                                      int t, int nb, int buf, int64_t plane, int row0, int nrows,
-                                      int j0, float dl, double& acc) {
+__device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
+                                      float (&tile)[2][kQ][kRows][kTileW],
+                                      float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows], int t,
+                                      int buf, float dl, double& acc) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
 
+  Group<MODE, kVec> g;
+  group_begin<MODE, kVec>(p, s, 4 * t + wave, lane, g);
+
   Raw<MODE> cur[kRows];
 #pragma unroll
   for (int m = 0; m < kRows; ++m) cur[m] = pre[m];
-  if (t + 1 < nb) {
+  // prefetch the next batch (rows past the segment are harmless: in range
+  // they are real pixels, out of range they read as 0)
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, c0, c1, col_ok, r0 + 10 + 4 * (t + 1) + m, pre[m]);
-  }
+  for (int m = 0; m < kRows; ++m) load_row<MODE>(s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
 
   // column pass
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
-    constexpr int kBase = 0;
     const int base = 4 * PH + m;  // compile-time after unrolling
-    (void)kBase;
     quantities<MODE>(cur[m], ring[(base + 10) % kRing]);
     float cs[kQ];
 #pragma unroll
@@ -365,33 +419,31 @@ __device__ __forceinline__ void batch(const Params& p, float (&tile)[2][kQ][kRow
   }
   __syncthreads();
 
-  // row pass: wave w -> batch row w; lane l -> outputs 4l .. 4l+3
-  const int ri = 4 * t + wave;
-  const int j = j0 + 4 * lane;
-  if (ri < nrows && lane < kRowLanes && j < p.out_w) {
-    float o[kQ][4];
+  // row pass: wave w -> batch row w; lane l -> outputs 4l .. 4l+3.  Lanes
+  // past the strip read the last real group and store out of range.
+  const int lr = lane < kRowLanes ? lane : kRowLanes - 1;
+  float o[kQ][4];
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const float* src = &tile[buf][q][wave][4 * lane];
-      float v[16];
+  for (int q = 0; q < kQ; ++q) {
+    const float* src = &tile[buf][q][wave][4 * lr];
+    float v[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
-        v[4 * k + 0] = f.x;
-        v[4 * k + 1] = f.y;
-        v[4 * k + 2] = f.z;
-        v[4 * k + 3] = f.w;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float s = tap(0) * v[u];
-#pragma unroll
-        for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), v[u + b], s);
-        o[q][u] = s;
-      }
+    for (int k = 0; k < 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+      v[4 * k + 0] = f.x;
+      v[4 * k + 1] = f.y;
+      v[4 * k + 2] = f.z;
+      v[4 * k + 3] = f.w;
     }
-    consume<MODE, kVec>(p, plane, row0 + ri, j, o, dl, acc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float a = tap(0) * v[u];
+#pragma unroll
+      for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
+      o[q][u] = a;
+    }
   }
+  consume<MODE, kVec>(p, s, g, o, dl, acc);
 }
 
 template <int MODE, bool kVec>
@@ -416,55 +468,66 @@ __global__ __launch_bounds__(kThreads) void ssim_strip_kernel(const Params p) {
   int buf = 0;
   const int64_t per_plane = (int64_t)p.strips * p.out_h;
   for (int64_t u = u_begin; u < u_end;) {
+    Seg<MODE> s;
     const int64_t plane = u / per_plane;
     const int64_t rem = u - plane * per_plane;
     const int strip = (int)(rem / p.out_h);
-    const int row0 = (int)(rem - (int64_t)strip * p.out_h);
+    s.row0 = (int)(rem - (int64_t)strip * p.out_h);
     const int64_t left = u_end - u;
-    const int nrows = (int)((int64_t)(p.out_h - row0) < left ? (int64_t)(p.out_h - row0) : left);
-    u += nrows;
-
-    const int j0 = strip * kStripOut;
-    const int c = j0 - p.off + tid;  // this lane's input column
-    const bool col_ok = (c >= 0) && (c < p.in_w);
-    const int cc = col_ok ? c : 0;
-    const float* c0;
-    const float* c1 = nullptr;
+    s.nrows = (int)((int64_t)(p.out_h - s.row0) < left ? (int64_t)(p.out_h - s.row0) : left);
+    u += s.nrows;
+    s.j0 = strip * kStripOut;
+    const int c = s.j0 - p.off + tid;  // this lane's input column
+    s.colbyte = (c >= 0 && c < p.in_w) ? (unsigned)c * 4u : kOob;
+    s.in_row = (unsigned)p.in_pitch * 4u;
+    s.r0 = s.row0 - p.off;
     if constexpr (MODE == kBwd) {
-      c0 = p.maps + plane * 4 * p.map_plane + cc;
+      const float* mp = p.maps + plane * 4 * p.map_plane;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s.in[k] = make_rsrc(mp + k * p.map_plane, p.map_plane * 4);
+      s.img[0] = make_rsrc(p.x + plane * p.img_plane, p.img_plane * 4);
+      s.img[1] = make_rsrc(p.y + plane * p.img_plane, p.img_plane * 4);
+      s.out[0] = make_rsrc(p.gx ? p.gx + plane * p.img_plane : p.x, p.gx ? p.img_plane * 4 : 0);
+      s.out[1] = make_rsrc(p.gy ? p.gy + plane * p.img_plane : p.y, p.gy ? p.img_plane * 4 : 0);
+      s.out_row = (unsigned)p.img_w * 4u;
     } else {
-      c0 = p.x + plane * p.in_plane + cc;
-      c1 = p.y + plane * p.in_plane + cc;
+      s.in[0] = make_rsrc(p.x + plane * p.in_plane, p.in_plane * 4);
+      s.in[1] = make_rsrc(p.y + plane * p.in_plane, p.in_plane * 4);
+      if constexpr (MODE == kFwdTrain) {
+        const float* mp = p.maps + plane * 4 * p.map_plane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s.out[k] = make_rsrc(mp + k * p.map_plane, p.map_plane * 4);
+      }
+      s.out_row = (unsigned)p.map_pitch * 4u;
     }
-    const int r0 = row0 - p.off;  // input row held by ring slot 0
-    const int nb = (nrows + kRows - 1) / kRows;
+    const int nb = (s.nrows + kRows - 1) / kRows;
 
     float ring[kRing][kQ];
     Raw<MODE> warm[10];
     Raw<MODE> pre[kRows];
 #pragma unroll
-    for (int k = 0; k < 10; ++k) load_row<MODE>(p, c0, c1, col_ok, r0 + k, warm[k]);
+    for (int k = 0; k < 10; ++k) load_row<MODE>(s, s.r0 + k, warm[k]);
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, c0, c1, col_ok, r0 + 10 + m, pre[m]);
+    for (int m = 0; m < kRows; ++m) load_row<MODE>(s, s.r0 + 10 + m, pre[m]);
 #pragma unroll
     for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], ring[k]);
 
     for (int t = 0;;) {
       if (t >= nb) break;
-      batch<MODE, kVec, 0>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      batch<MODE, kVec, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, 1>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      batch<MODE, kVec, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, 2>(p, tile, ring, pre, c0, c1, col_ok, r0, t, nb, buf, plane, row0, nrows, j0, dl, acc);
+      batch<MODE, kVec, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       ++t;
     }
   }
 
   if constexpr (MODE != kBwd) {
-    // workgroup sum of the SSIM map, then the last workgroup finishes the mean
+    // workgroup sum of the map of 1 - S, then the last workgroup finishes the mean
     const int wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
@@ -474,20 +537,26 @@ __global__ __launch_bounds__(kThreads) void ssim_strip_kernel(const Params p) {
       double bs = 0.0;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) bs += red[w];
+      // Publish the partial with a device-coherent atomic store and wait for
+      // its acknowledgement before taking the ticket: a release of exactly
+      // this one value.  (A release fence would also write back every dirty
+      // line of this XCD's L2 -- megabytes of map stores -- in every
+      // workgroup.)
       __hip_atomic_store(&p.ws->partial[blockIdx.x], bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
       const unsigned prev =
-          __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       is_last = (prev == (unsigned)(G - 1));
     }
     __syncthreads();
     if (is_last && wave == 0) {
-      double s = 0.0;
+      double sum = 0.0;
       for (int k = lane; k < G; k += kWave)
-        s += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sum += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+      for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
       if (lane == 0) {
-        *p.loss = (float)(s * p.inv_m);
+        *p.loss = (float)(sum * p.inv_m);
         __hip_atomic_store(&p.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -558,10 +627,13 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, Shape* 
   const int64_t Ho = padding == SSIM_PAD_VALID ? H - 10 : H;
   const int64_t Wo = padding == SSIM_PAD_VALID ? W - 10 : W;
   if (Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
-  const int64_t lim = (int64_t)1 << 31;
-  if (H > lim / W) return SSIM_ERR_OVERFLOW;
+  // Buffer offsets are 32-bit: a plane (image or map) holds at most 2^27
+  // elements and a row at most 2^20, so valid offsets stay below 2^29 and the
+  // out-of-range ones (negative rows, the 2^31 marker) stay above 2^30.
+  const int64_t lim = (int64_t)1 << 27;
+  if (W > ((int64_t)1 << 20) || H > lim / W) return SSIM_ERR_OVERFLOW;
   const int64_t pitch = roundup4(Wo);
-  if (Ho > (lim - 1) / pitch || H * W >= lim || Ho * pitch >= lim) return SSIM_ERR_OVERFLOW;
+  if (H * W > lim || Ho * pitch > lim) return SSIM_ERR_OVERFLOW;
   if (N > (int64_t)1 << 40 || C > ((int64_t)1 << 40) / N) return SSIM_ERR_OVERFLOW;
   const int64_t planes = N * C;
   // bytes must fit comfortably in 64 bits
@@ -612,7 +684,7 @@ const char* ssim_strerror(int code) {
     case SSIM_ERR_NULL: return "a required pointer is NULL";
     case SSIM_ERR_SHAPE: return "bad shape: N, C, H, W must be positive and valid padding needs H, W >= 11";
     case SSIM_ERR_PADDING: return "padding must be SSIM_PAD_VALID (0) or SSIM_PAD_SAME (1)";
-    case SSIM_ERR_OVERFLOW: return "a plane holds 2^31 or more elements, or a size overflows";
+    case SSIM_ERR_OVERFLOW: return "a plane holds more than 2^27 elements, a row more than 2^20, or a size overflows";
     case SSIM_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case SSIM_ERR_HIP: return "a HIP runtime call failed";
     case SSIM_ERR_DEVICE: return "the current device is not a wave64 gfx950 GPU";

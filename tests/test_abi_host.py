@@ -83,7 +83,8 @@ def test_forward_argument_errors_return_before_any_hip_call():
     assert _fwd(lib, C=-1) == -2
     assert _fwd(lib, H=10) == -2          # valid needs H >= 11
     assert _fwd(lib, W=10) == -2
-    assert _fwd(lib, H=1 << 16, W=1 << 16) == -4   # a plane of 2^32 elements
+    assert _fwd(lib, H=1 << 14, W=1 << 14) == -4   # a plane of 2^28 elements
+    assert _fwd(lib, H=11, W=(1 << 20) + 1) == -4  # a row longer than 2^20
     assert _fwd(lib, maps=0x300004) == -2          # saved maps must be 16-byte aligned
     assert _fwd(lib, loss=0x1000 + 64) == -5       # loss inside img1
     assert _fwd(lib, maps=0x100000 + 4096) == -5   # maps overlap img2
