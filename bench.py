@@ -6,10 +6,11 @@ resident in HBM, through the C ABI on torch's current stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Prints one JSON line: metric Mpix/s (pixels = N*H*W per step), the roofline
-of the dominant kernel (algorithmic bytes per launch / average launch time
-from HIP events recorded around every launch of the timed region), and the
-fp64 CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line: metric Mpix/s (pixels = N*H*W per step, wall clock over
+K steps), the roofline of the dominant kernel (algorithmic bytes per launch /
+average launch time from HIP events around K back-to-back launches of that
+kernel on the stream it runs on), and the fp64 CPU oracle's throughput on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PAGES_MPIX_S = 1920 * 1080 / 7.2e-3 / 1e6  # the pages' 7.2 ms fwd+bwd at 1080p (RDNA4 R9700)
 KERNEL_SRC = os.path.join(ROOT, "ssim_loss_amd", "csrc", "ssim_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -125,24 +126,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # the step: K forward+backward pairs, wall clock between two synchronisations
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(K):
-        ev[k][0].record()
-        S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
-        ev[k][1].record()
-        S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
-        ev[k][2].record()
+    for _ in range(K):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     ms_per_step = elapsed * 1e3 / K
     mpix = N * H * W / 1e6
     value = mpix * K / elapsed
+
+    # per-kernel launch time: K launches of one kernel back to back between two
+    # HIP events on the stream the kernels run on (torch's current stream)
+    def per_launch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    fwd_ms = per_launch_ms(lambda: S.ssim_forward(t1, t2, w.padding, loss, maps, ws))
+    bwd_ms = per_launch_ms(lambda: S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2))
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
@@ -177,9 +185,13 @@ def main():
     dom = max(kern, key=kern.get)
     achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
 
+    # HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    # WRITE_SIZE, scaled by a copy kernel of known size), valid only for the
+    # kernel source they were taken from
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    traffic_file = os.path.join(PROFILES, f"hbm_traffic_{args.workload}.json")
+    if os.path.exists(traffic_file):
+        with open(traffic_file) as f:
             tr = json.load(f)
         if (tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload
                 and dom in tr.get("bytes_per_launch", {})):

@@ -447,7 +447,7 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
 }
 
 template <int MODE, bool kVec>
-__global__ __launch_bounds__(kThreads) void ssim_strip_kernel(const Params p) {
+__device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kTileW];
   __shared__ double red[kWaves];
   __shared__ int is_last;
@@ -563,6 +563,20 @@ __global__ __launch_bounds__(kThreads) void ssim_strip_kernel(const Params p) {
   }
 }
 
+// Entry kernels (one per direction and mode; named for profiles).
+__global__ __launch_bounds__(kThreads) void ssim_fwd_infer_kernel(const Params p) {
+  strip_body<kFwdInfer, false>(p);
+}
+__global__ __launch_bounds__(kThreads) void ssim_fwd_train_kernel(const Params p) {
+  strip_body<kFwdTrain, false>(p);
+}
+__global__ __launch_bounds__(kThreads) void ssim_bwd_kernel(const Params p) {
+  strip_body<kBwd, true>(p);
+}
+__global__ __launch_bounds__(kThreads) void ssim_bwd_unaligned_kernel(const Params p) {
+  strip_body<kBwd, false>(p);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 
@@ -590,10 +604,8 @@ int device_info(const DeviceInfo** out) {
       d.status = SSIM_ERR_DEVICE;
     } else {
       d.cus = prop.multiProcessorCount;
-      const void* ks[4] = {(const void*)ssim_strip_kernel<kFwdInfer, false>,
-                           (const void*)ssim_strip_kernel<kFwdTrain, false>,
-                           (const void*)ssim_strip_kernel<kBwd, true>,
-                           (const void*)ssim_strip_kernel<kBwd, false>};
+      const void* ks[4] = {(const void*)ssim_fwd_infer_kernel, (const void*)ssim_fwd_train_kernel,
+                           (const void*)ssim_bwd_kernel, (const void*)ssim_bwd_unaligned_kernel};
       for (int k = 0; k < 4; ++k) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ks[k], kThreads, 0) != hipSuccess)
@@ -757,9 +769,9 @@ int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int
   const int G = grid_for(d, which, p.units);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (saved_maps)
-    hipLaunchKernelGGL((ssim_strip_kernel<kFwdTrain, false>), dim3(G), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(ssim_fwd_train_kernel, dim3(G), dim3(kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((ssim_strip_kernel<kFwdInfer, false>), dim3(G), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(ssim_fwd_infer_kernel, dim3(G), dim3(kThreads), 0, st, p);
   return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
@@ -805,9 +817,9 @@ int ssim_backward(const float* dloss, const float* img1, const float* img2, int6
   const int G = grid_for(d, vec ? 2 : 3, p.units);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (vec)
-    hipLaunchKernelGGL((ssim_strip_kernel<kBwd, true>), dim3(G), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(ssim_bwd_kernel, dim3(G), dim3(kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((ssim_strip_kernel<kBwd, false>), dim3(G), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(ssim_bwd_unaligned_kernel, dim3(G), dim3(kThreads), 0, st, p);
   return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
