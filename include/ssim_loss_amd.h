@@ -52,8 +52,8 @@ enum {
   SSIM_ERR_NULL = -1,     /* a required pointer is NULL */
   SSIM_ERR_SHAPE = -2,    /* N, C, H or W <= 0, or valid padding with H < 11 or W < 11 */
   SSIM_ERR_PADDING = -3,  /* padding is neither SSIM_PAD_VALID nor SSIM_PAD_SAME */
-  SSIM_ERR_OVERFLOW = -4, /* a plane (image or map) holds more than 2^27 elements, a row
-                             more than 2^20, or a buffer size overflows */
+  SSIM_ERR_OVERFLOW = -4, /* a plane (image, or map with its row pitch) holds more than
+                             2^27 elements, a row more than 2^20, or a size overflows */
   SSIM_ERR_ALIAS = -5,    /* an output buffer overlaps an input or another output */
   SSIM_ERR_HIP = -6,      /* a HIP runtime call failed (launch, device query) */
   SSIM_ERR_DEVICE = -7    /* the current device is not a wave64 gfx9 GPU */
@@ -77,8 +77,8 @@ void ssim_taps(float out[11]);
 int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo);
 
 /* Bytes of the saved-maps buffer ssim_forward writes in training mode and
- * ssim_backward reads: four fp32 maps per plane, each Ho rows with a row
- * pitch of Wo rounded up to a multiple of 4 floats, i.e.
+ * ssim_backward reads: four fp32 map planes per image plane, each Ho rows
+ * with a row pitch of Wo rounded up to a multiple of 4 floats, i.e.
  * 16 * N*C * Ho * roundup(Wo, 4) bytes.  The buffer must be 16-byte
  * aligned.  Returns 0 for invalid arguments.  Host-only. */
 size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding);
@@ -94,18 +94,17 @@ size_t ssim_workspace_bytes(void);
  * of SSIM, M = N*C*Ho*Wo, and writes it as one fp32 to `loss` (device).
  *
  *   img1, img2  : fp32 NCHW device images (inputs, not modified)
- *   N, C, H, W  : shape; a plane holds at most 2^27 elements (and its
- *                 map, Ho rows of roundup(Wo, 4), as well), a row at most
- *                 2^20; N*C is unbounded
+ *   N, C, H, W  : shape; a plane holds at most 2^27 elements (its map
+ *                 too, with Wo rounded up to 4) and a row at most 2^20;
+ *                 N*C is unbounded
  *   padding     : SSIM_PAD_VALID or SSIM_PAD_SAME
  *   loss        : device fp32 scalar (output)
  *   saved_maps  : NULL for inference (no gradient will be taken), else a
  *                 device buffer of ssim_saved_maps_bytes(...) bytes that
- *                 receives, at every map entry, the partial derivatives of
- *                 the loss with respect to the four blurred quantities the
- *                 kernels form -- B(x - 1/2), B(y - 1/2), B((x - y)^2) (times
- *                 2) and B((x - 1/2)(y - 1/2)) -- as four planes per image
- *                 plane; ssim_backward consumes them.
+ *                 receives, at every map entry, the four blurred quantities
+ *                 the kernels form -- B(x - 1/2), B(y - 1/2), B((x - y)^2)
+ *                 and B((x - 1/2)(y - 1/2)) -- one map plane each;
+ *                 ssim_backward forms the loss partials from them.
  *   workspace   : device buffer of ssim_workspace_bytes() bytes, zeroed
  *                 before its first use
  *   stream      : hipStream_t (NULL = default stream)

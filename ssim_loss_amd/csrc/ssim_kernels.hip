@@ -23,7 +23,7 @@
 //     near 1, the end of a training run) keep full relative accuracy in
 //     1 - S, which is what the loss sums.
 //   * The pages send five upstream gradients through B^T (mu1, mu2, s11, s22,
-//     s12); in the basis above there are four maps, m0..m3 = d loss /
+//     s12); in the basis above there are four, m0..m3 = d loss /
 //     d(mu_x', mu_y', R, P') (R's with the chain rule's 2 folded in), and
 //         grad_x = dloss * (B^T m0 + y' * B^T m3 + (x - y) * B^T m2)
 //         grad_y = dloss * (B^T m1 + x' * B^T m3 - (x - y) * B^T m2).
@@ -48,9 +48,13 @@
 //                 takes row w of the batch and lane l produces the 4 adjacent
 //                 outputs 4l..4l+3 from 4 aligned 16-byte LDS reads per
 //                 quantity (conflict-free: lanes read consecutive 16 bytes).
-//   consumer    : forward -> SSIM, loss partial sum, 4 map stores (16 bytes
-//                 each, one per map plane); backward -> chain rule and two
-//                 gradient stores.
+//   consumer    : forward -> 1 - SSIM into the loss sum and, in training
+//                 mode, the four blurred quantities stored as four map planes
+//                 (16 bytes per plane per lane); backward -> chain rule and
+//                 two gradient stores.  The backward's column pass forms the
+//                 loss partials from the saved quantities as it reads them:
+//                 the forward is ALU-bound and the backward memory-bound, so
+//                 the partials' arithmetic sits where it is free.
 // Work is split into (plane, strip, output row) units; each workgroup takes
 // an equal contiguous range of units (a persistent-style grid of about one
 // wave of resident workgroups), marching down its strips so that every
@@ -147,7 +151,7 @@ struct Params {
   // maps (fwd: written in training mode; bwd: the blurred input)
   float* maps;
   int map_pitch;        // roundup(Wo, 4)
-  int64_t map_plane;    // Ho * map_pitch
+  int64_t map_plane;    // Ho * map_pitch floats per map plane
   // forward
   float k_m2;           // -2 / M
   double inv_m;         // 1 / M
@@ -186,12 +190,74 @@ __device__ __forceinline__ float ld1(rsrc_t r, unsigned off) {
 __device__ __forceinline__ float4 ld4(rsrc_t r, unsigned off) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Stores take a cache policy: kNt marks them non-temporal (streaming), for
+// launches whose data cannot stay in the last-level cache anyway.
+constexpr int kPolicyNt = 2;  // gfx950 cache-policy bit: non-temporal
+template <bool kNt>
 __device__ __forceinline__ void st1(rsrc_t r, unsigned off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kNt ? kPolicyNt : 0);
 }
+template <bool kNt>
 __device__ __forceinline__ void st4(rsrc_t r, unsigned off, float4 v) {
   using u4 = unsigned __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kNt ? kPolicyNt : 0);
+}
+
+// ---------------------------------------------------------------------------
+// SSIM at one map position
+
+// The SSIM terms at one map position, from the blurred quantities
+// mu_x', mu_y', R = B((x-y)^2), P' = B(x' y').
+struct SsimTerms {
+  float mux, muy, dm, a1, d1, b1, a2, d2, b2, inv;
+};
+
+__device__ __forceinline__ SsimTerms ssim_terms(float mxs, float mys, float rr, float pp) {
+  SsimTerms t;
+  t.mux = mxs + kShift;
+  t.muy = mys + kShift;
+  t.dm = mxs - mys;
+  t.a1 = __builtin_fmaf(2.0f * t.mux, t.muy, kC1);
+  t.d1 = t.dm * t.dm;
+  t.b1 = t.a1 + t.d1;
+  const float cov = __builtin_fmaf(-mxs, mys, pp);
+  t.a2 = __builtin_fmaf(2.0f, cov, kC2);
+  t.d2 = __builtin_fmaf(-t.dm, t.dm, rr);
+  t.b2 = t.a2 + t.d2;
+  t.inv = __builtin_amdgcn_rcpf(t.b1 * t.b2);
+  return t;
+}
+
+// 1 - S = (A1 D2 + D1 B2) / (B1 B2)
+__device__ __forceinline__ float one_minus_ssim(const SsimTerms& t) {
+  return __builtin_fmaf(t.a1, t.d2, t.d1 * t.b2) * t.inv;
+}
+
+// The four loss partials at one map position (k_m2 = -2/M).  With
+// S = A1 A2 inv, inv = 1/(B1 B2), and every term a multiple of D1, D2 or dmu
+// (so all vanish when x = y):
+//   dS/dmu_x' = 2 inv (mu_y T1 - mu_y' T2 + T3)
+//   dS/dmu_y' = 2 inv (mu_x T1 - mu_x' T2 - T3)
+//   dS/dP'    = 2 inv T2,      dS/dR = -S / B2 = -S B1 inv
+// where T1 = A2 D1 / B1, T2 = A1 D2 / B2, T3 = S (B1 - B2) dmu.
+// Maps (loss = mean of 1 - S over M entries, k = -(2/M) inv):
+//   m0 = -(1/M) dS/dmu_x' = k (mu_y T1 - mu_y' T2 + T3)
+//   m1 = -(1/M) dS/dmu_y' = k (mu_x T1 - mu_x' T2 - T3)
+//   m2 = -(2/M) dS/dR     = -k S B1   (the chain rule's 2 folded in)
+//   m3 = -(1/M) dS/dP'    = k T2
+__device__ __forceinline__ void loss_partials(float mxs, float mys, const SsimTerms& t, float k_m2,
+                                              float (&m)[4]) {
+  const float s = t.a1 * t.a2 * t.inv;
+  const float ib1 = t.b2 * t.inv;
+  const float ib2 = t.b1 * t.inv;
+  const float t1 = t.a2 * t.d1 * ib1;
+  const float t2 = t.a1 * t.d2 * ib2;
+  const float t3 = s * (t.b1 - t.b2) * t.dm;
+  const float k = k_m2 * t.inv;
+  m[0] = k * __builtin_fmaf(t.muy, t1, __builtin_fmaf(-mys, t2, t3));
+  m[1] = k * __builtin_fmaf(t.mux, t1, __builtin_fmaf(-mxs, t2, -t3));
+  m[2] = -(k * s) * t.b1;
+  m[3] = k * t2;
 }
 
 // ---------------------------------------------------------------------------
@@ -206,30 +272,47 @@ struct Seg {
   unsigned colbyte;     // this lane's input column in bytes, or kOob
   unsigned in_row;      // input row pitch, bytes
   unsigned out_row;     // output row pitch, bytes
+  unsigned out_elem;    // bytes per output element (4)
   int r0;               // input row held by ring slot 0 (first output row - off)
   int row0, nrows;      // output rows [row0, row0 + nrows)
   int j0;               // first output column of the strip
 };
 
 template <int MODE>
-struct Raw { float v[Seg<MODE>::kIn]; };
+struct Raw {
+  float v[4];  // fwd: x, y; bwd: the four blurred quantities of a map entry
+  bool in;     // the element lies inside the input extent
+};
 
 // This lane's input pixel(s) in input row r; 0 outside the input extent.
 template <int MODE>
-__device__ __forceinline__ void load_row(const Seg<MODE>& s, int r, Raw<MODE>& out) {
+__device__ __forceinline__ void load_row(const Params& p, const Seg<MODE>& s, int r,
+                                         Raw<MODE>& out) {
   const unsigned off = s.colbyte + (unsigned)r * s.in_row;
+  if constexpr (MODE == kBwd) {
 #pragma unroll
-  for (int k = 0; k < Seg<MODE>::kIn; ++k) out.v[k] = ld1(s.in[k], off);
+    for (int k = 0; k < 4; ++k) out.v[k] = ld1(s.in[k], off);
+  } else {
+    out.v[0] = ld1(s.in[0], off);
+    out.v[1] = ld1(s.in[1], off);
+  }
+  out.in = (s.colbyte != kOob) && ((unsigned)r < (unsigned)p.in_h);
 }
 
 // Quantities blurred by the forward: x', y', (x - y)^2 and x' y' with
-// x' = x - 1/2, y' = y - 1/2.  The backward blurs its four maps as they are.
+// x' = x - 1/2, y' = y - 1/2.  Quantities blurred by the backward: the four
+// loss partials at each map entry, formed from the saved blurred quantities.
 template <int MODE>
-__device__ __forceinline__ void quantities(const Raw<MODE>& r, float (&q)[kQ]) {
+__device__ __forceinline__ void quantities(const Raw<MODE>& r, float k_m2, float (&q)[kQ]) {
   if constexpr (MODE == kBwd) {
+    // the loss partials at this map entry; zero outside the map (the
+    // adjoint's zero fill)
+    float m[4];
+    loss_partials(r.v[0], r.v[1], ssim_terms(r.v[0], r.v[1], r.v[2], r.v[3]), k_m2, m);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = r.v[k];
+    for (int k = 0; k < 4; ++k) q[k] = r.in ? m[k] : 0.0f;
   } else {
+    (void)k_m2;
     const float x = r.v[0] - kShift, y = r.v[1] - kShift;
     const float d = r.v[0] - r.v[1];
     q[0] = x;
@@ -242,55 +325,6 @@ __device__ __forceinline__ void quantities(const Raw<MODE>& r, float (&q)[kQ]) {
 // ---------------------------------------------------------------------------
 // Consumers (4 adjacent outputs of one row)
 
-// 1 - SSIM and the four loss partials at one map position, from the blurred
-// quantities mu_x', mu_y', R = B((x-y)^2), P' = B(x' y').
-struct SsimOut {
-  float ell;   // 1 - S
-  float m[4];  // loss partials (training mode)
-};
-
-template <bool kTrain>
-__device__ __forceinline__ SsimOut ssim_point(float mxs, float mys, float rr, float pp,
-                                              float k_m2) {
-  SsimOut o;
-  const float mux = mxs + kShift, muy = mys + kShift;
-  const float dm = mxs - mys;
-  const float a1 = __builtin_fmaf(2.0f * mux, muy, kC1);
-  const float d1 = dm * dm;
-  const float b1 = a1 + d1;
-  const float cov = __builtin_fmaf(-mxs, mys, pp);
-  const float a2 = __builtin_fmaf(2.0f, cov, kC2);
-  const float d2 = __builtin_fmaf(-dm, dm, rr);
-  const float b2 = a2 + d2;
-  const float inv = __builtin_amdgcn_rcpf(b1 * b2);
-  o.ell = __builtin_fmaf(a1, d2, d1 * b2) * inv;
-  if constexpr (kTrain) {
-    // With S = A1 A2 inv, inv = 1/(B1 B2), and every term a multiple of D1,
-    // D2 or dmu (so all vanish when x = y):
-    //   dS/dmu_x' = 2 inv (mu_y T1 - mu_y' T2 + T3)
-    //   dS/dmu_y' = 2 inv (mu_x T1 - mu_x' T2 - T3)
-    //   dS/dP'    = 2 inv T2,      dS/dR = -S / B2 = -S B1 inv
-    // where T1 = A2 D1 / B1, T2 = A1 D2 / B2, T3 = S (B1 - B2) dmu.
-    // Maps (loss = mean of 1 - S over M entries, k = -(2/M) inv):
-    //   m0 = -(1/M) dS/dmu_x' = k (mu_y T1 - mu_y' T2 + T3)
-    //   m1 = -(1/M) dS/dmu_y' = k (mu_x T1 - mu_x' T2 - T3)
-    //   m2 = -(2/M) dS/dR     = -k S B1
-    //   m3 = -(1/M) dS/dP'    = k T2
-    const float s = a1 * a2 * inv;
-    const float ib1 = b2 * inv;
-    const float ib2 = b1 * inv;
-    const float t1 = a2 * d1 * ib1;
-    const float t2 = a1 * d2 * ib2;
-    const float t3 = s * (b1 - b2) * dm;
-    const float k = k_m2 * inv;
-    o.m[0] = k * __builtin_fmaf(muy, t1, __builtin_fmaf(-mys, t2, t3));
-    o.m[1] = k * __builtin_fmaf(mux, t1, __builtin_fmaf(-mxs, t2, -t3));
-    o.m[2] = -(k * s) * b1;
-    o.m[3] = k * t2;
-  }
-  return o;
-}
-
 // Where this lane's output group lives: byte offset of its first output in
 // the output planes, or kOob when the group is not real (row outside the
 // segment, lane outside the strip, first column outside the output extent).
@@ -301,7 +335,7 @@ struct Group {
   bool ok;
   int j;
   unsigned base;
-  unsigned off[4];  // scalar path: per-output offsets
+  unsigned off[4];  // per-output offsets (kOob past the output extent)
   float xv[4], yv[4];
 };
 
@@ -310,7 +344,10 @@ __device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s,
                                             Group<MODE, kVec>& g) {
   g.j = s.j0 + 4 * lane;
   g.ok = (ri < s.nrows) && (lane < kRowLanes) && (g.j < p.out_w);
-  g.base = g.ok ? (unsigned)(s.row0 + ri) * s.out_row + (unsigned)g.j * 4u : kOob;
+  g.base = g.ok ? (unsigned)(s.row0 + ri) * s.out_row + (unsigned)g.j * s.out_elem : kOob;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    g.off[t] = (g.ok && (g.j + t) < p.out_w) ? g.base + s.out_elem * t : kOob;
   if constexpr (MODE == kBwd) {
     if constexpr (kVec) {
       const float4 a = ld4(s.img[0], g.base);
@@ -320,7 +357,6 @@ __device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s,
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        g.off[t] = (g.ok && (g.j + t) < p.out_w) ? g.base + 4u * t : kOob;
         g.xv[t] = ld1(s.img[0], g.off[t]);
         g.yv[t] = ld1(s.img[1], g.off[t]);
       }
@@ -328,30 +364,27 @@ __device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s,
   }
 }
 
-template <int MODE, bool kVec>
+template <int MODE, bool kVec, bool kNt>
 __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
                                         const Group<MODE, kVec>& g, const float (&o)[kQ][4],
                                         float dl, double& acc) {
   if constexpr (MODE != kBwd) {
-    constexpr bool kTrain = (MODE == kFwdTrain);
     float s4 = 0.0f;
-    float m[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const SsimOut r = ssim_point<kTrain>(o[0][t], o[1][t], o[2][t], o[3][t], p.k_m2);
-      s4 += (g.ok && (g.j + t) < p.out_w) ? r.ell : 0.0f;
-      if constexpr (kTrain) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m[k][t] = r.m[k];
-      }
+      const float ell = one_minus_ssim(ssim_terms(o[0][t], o[1][t], o[2][t], o[3][t]));
+      s4 += (g.ok && (g.j + t) < p.out_w) ? ell : 0.0f;
     }
     acc += (double)s4;
-    if constexpr (kTrain) {
-      // j is a multiple of 4 and the pitch rounds Wo up to one, so the whole
-      // group lies inside the padded row; entries past Wo land in the pitch
-      // padding, which nothing reads.
+    if constexpr (MODE == kFwdTrain) {
+      // training: save the four blurred quantities, one map plane each (a
+      // lane's 4 outputs are 16 contiguous bytes of a plane, so a wave writes
+      // 1 KiB per plane per instruction); the backward forms the loss
+      // partials from them as it reads them.  j is a multiple of 4 and the
+      // pitch rounds Wo up to one, so the whole group lies inside the padded
+      // row (entries past Wo land in the padding, which nothing reads).
 #pragma unroll
-      for (int k = 0; k < 4; ++k) st4(s.out[k], g.base, make_float4(m[k][0], m[k][1], m[k][2], m[k][3]));
+      for (int q = 0; q < 4; ++q) st4<kNt>(s.out[q], g.base, make_float4(o[q][0], o[q][1], o[q][2], o[q][3]));
     }
   } else {
     float g1[4], g2[4];
@@ -365,13 +398,13 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
     // a gradient the caller does not want has a zero-size descriptor: its
     // stores are dropped without a branch
     if constexpr (kVec) {
-      st4(s.out[0], g.base, make_float4(g1[0], g1[1], g1[2], g1[3]));
-      st4(s.out[1], g.base, make_float4(g2[0], g2[1], g2[2], g2[3]));
+      st4<kNt>(s.out[0], g.base, make_float4(g1[0], g1[1], g1[2], g1[3]));
+      st4<kNt>(s.out[1], g.base, make_float4(g2[0], g2[1], g2[2], g2[3]));
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        st1(s.out[0], g.off[t], g1[t]);
-        st1(s.out[1], g.off[t], g2[t]);
+        st1<kNt>(s.out[0], g.off[t], g1[t]);
+        st1<kNt>(s.out[1], g.off[t], g2[t]);
       }
     }
   }
@@ -382,7 +415,7 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
 // the row pass and the consumer.  PH = batch index mod 3 fixes the ring slots
 // at compile time.
 
-template <int MODE, bool kVec, int PH>
+template <int MODE, bool kVec, bool kNt, int PH>
 __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
                                       float (&tile)[2][kQ][kRows][kTileW],
                                       float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows], int t,
@@ -400,13 +433,13 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
   // prefetch the next batch (rows past the segment are harmless: in range
   // they are real pixels, out of range they read as 0)
 #pragma unroll
-  for (int m = 0; m < kRows; ++m) load_row<MODE>(s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
+  for (int m = 0; m < kRows; ++m) load_row<MODE>(p, s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
 
   // column pass
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
     const int base = 4 * PH + m;  // compile-time after unrolling
-    quantities<MODE>(cur[m], ring[(base + 10) % kRing]);
+    quantities<MODE>(cur[m], p.k_m2, ring[(base + 10) % kRing]);
     float cs[kQ];
 #pragma unroll
     for (int q = 0; q < kQ; ++q) cs[q] = tap(0) * ring[base % kRing][q];
@@ -422,7 +455,7 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
   // row pass: wave w -> batch row w; lane l -> outputs 4l .. 4l+3.  Lanes
   // past the strip read the last real group and store out of range.
   const int lr = lane < kRowLanes ? lane : kRowLanes - 1;
-  float o[kQ][4];
+  float o[kQ][4];  // [quantity][output]: the 4 outputs of a map plane are one register quad
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     const float* src = &tile[buf][q][wave][4 * lr];
@@ -443,10 +476,10 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
       o[q][u] = a;
     }
   }
-  consume<MODE, kVec>(p, s, g, o, dl, acc);
+  consume<MODE, kVec, kNt>(p, s, g, o, dl, acc);
 }
 
-template <int MODE, bool kVec>
+template <int MODE, bool kVec, bool kNt>
 __device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kTileW];
   __shared__ double red[kWaves];
@@ -490,6 +523,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
       s.out[0] = make_rsrc(p.gx ? p.gx + plane * p.img_plane : p.x, p.gx ? p.img_plane * 4 : 0);
       s.out[1] = make_rsrc(p.gy ? p.gy + plane * p.img_plane : p.y, p.gy ? p.img_plane * 4 : 0);
       s.out_row = (unsigned)p.img_w * 4u;
+      s.out_elem = 4u;
     } else {
       s.in[0] = make_rsrc(p.x + plane * p.in_plane, p.in_plane * 4);
       s.in[1] = make_rsrc(p.y + plane * p.in_plane, p.in_plane * 4);
@@ -499,6 +533,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
         for (int k = 0; k < 4; ++k) s.out[k] = make_rsrc(mp + k * p.map_plane, p.map_plane * 4);
       }
       s.out_row = (unsigned)p.map_pitch * 4u;
+      s.out_elem = 4u;
     }
     const int nb = (s.nrows + kRows - 1) / kRows;
 
@@ -506,21 +541,21 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     Raw<MODE> warm[10];
     Raw<MODE> pre[kRows];
 #pragma unroll
-    for (int k = 0; k < 10; ++k) load_row<MODE>(s, s.r0 + k, warm[k]);
+    for (int k = 0; k < 10; ++k) load_row<MODE>(p, s, s.r0 + k, warm[k]);
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) load_row<MODE>(s, s.r0 + 10 + m, pre[m]);
+    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, s, s.r0 + 10 + m, pre[m]);
 #pragma unroll
-    for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], ring[k]);
+    for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], p.k_m2, ring[k]);
 
     for (int t = 0;;) {
       if (t >= nb) break;
-      batch<MODE, kVec, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       ++t;
     }
@@ -563,28 +598,48 @@ __device__ __forceinline__ void strip_body(const Params& p) {
   }
 }
 
-// Entry kernels (one per direction and mode; named for profiles).
+// Entry kernels (one per direction, mode and store policy; named for
+// profiles).  "stream" kernels mark their stores non-temporal.
 __global__ __launch_bounds__(kThreads) void ssim_fwd_infer_kernel(const Params p) {
-  strip_body<kFwdInfer, false>(p);
+  strip_body<kFwdInfer, false, false>(p);
 }
 __global__ __launch_bounds__(kThreads) void ssim_fwd_train_kernel(const Params p) {
-  strip_body<kFwdTrain, false>(p);
+  strip_body<kFwdTrain, false, false>(p);
+}
+__global__ __launch_bounds__(kThreads) void ssim_fwd_train_stream_kernel(const Params p) {
+  strip_body<kFwdTrain, false, true>(p);
 }
 __global__ __launch_bounds__(kThreads) void ssim_bwd_kernel(const Params p) {
-  strip_body<kBwd, true>(p);
+  strip_body<kBwd, true, false>(p);
+}
+__global__ __launch_bounds__(kThreads) void ssim_bwd_stream_kernel(const Params p) {
+  strip_body<kBwd, true, true>(p);
 }
 __global__ __launch_bounds__(kThreads) void ssim_bwd_unaligned_kernel(const Params p) {
-  strip_body<kBwd, false>(p);
+  strip_body<kBwd, false, false>(p);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 
+enum KernelId { kKFwdInfer, kKFwdTrain, kKFwdTrainStream, kKBwd, kKBwdStream, kKBwdUnaligned, kKernels };
+const void* const kKernelTable[kKernels] = {
+    (const void*)ssim_fwd_infer_kernel, (const void*)ssim_fwd_train_kernel,
+    (const void*)ssim_fwd_train_stream_kernel, (const void*)ssim_bwd_kernel,
+    (const void*)ssim_bwd_stream_kernel, (const void*)ssim_bwd_unaligned_kernel};
+
+// Bytes a training step touches in HBM (both images, the saved maps, both
+// gradients).  Above this the step cannot stay in the 256 MB last-level
+// cache between the forward and the backward, and the stores stream
+// (non-temporal); below it they stay cacheable so that the backward finds
+// the maps there.
+constexpr size_t kStreamBytes = (size_t)256 << 20;
+
 struct DeviceInfo {
   bool ready = false;
   int status = SSIM_OK;
   int cus = 0;
-  int occ[4] = {0, 0, 0, 0};  // resident workgroups per CU: fwd-infer, fwd-train, bwd-vec, bwd-scalar
+  int occ[kKernels] = {};  // resident workgroups per CU, per entry kernel
 };
 
 constexpr int kMaxDevices = 64;
@@ -604,11 +659,9 @@ int device_info(const DeviceInfo** out) {
       d.status = SSIM_ERR_DEVICE;
     } else {
       d.cus = prop.multiProcessorCount;
-      const void* ks[4] = {(const void*)ssim_fwd_infer_kernel, (const void*)ssim_fwd_train_kernel,
-                           (const void*)ssim_bwd_kernel, (const void*)ssim_bwd_unaligned_kernel};
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kKernels; ++k) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ks[k], kThreads, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kKernelTable[k], kThreads, 0) != hipSuccess)
           return SSIM_ERR_HIP;
         d.occ[k] = n > 0 ? n : 1;
       }
@@ -639,9 +692,11 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, Shape* 
   const int64_t Ho = padding == SSIM_PAD_VALID ? H - 10 : H;
   const int64_t Wo = padding == SSIM_PAD_VALID ? W - 10 : W;
   if (Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
-  // Buffer offsets are 32-bit: a plane (image or map) holds at most 2^27
-  // elements and a row at most 2^20, so valid offsets stay below 2^29 and the
-  // out-of-range ones (negative rows, the 2^31 marker) stay above 2^30.
+  // Buffer offsets are 32-bit: a plane (image, or map with its row pitch)
+  // holds at most 2^27 elements and a row at most 2^20, so valid offsets
+  // stay below 2^29 and the out-of-range ones (rows above the plane wrap to
+  // just below 2^32; the 2^31 marker plus at most 14 rows of 4 MiB) stay
+  // above 2^30.
   const int64_t lim = (int64_t)1 << 27;
   if (W > ((int64_t)1 << 20) || H > lim / W) return SSIM_ERR_OVERFLOW;
   const int64_t pitch = roundup4(Wo);
@@ -765,13 +820,13 @@ int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int
   p.loss = loss;
   p.ws = static_cast<Workspace*>(workspace);
 
-  const int which = saved_maps ? 1 : 0;
+  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
+  const int which = !saved_maps ? kKFwdInfer : stream_st ? kKFwdTrainStream : kKFwdTrain;
   const int G = grid_for(d, which, p.units);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (saved_maps)
-    hipLaunchKernelGGL(ssim_fwd_train_kernel, dim3(G), dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(ssim_fwd_infer_kernel, dim3(G), dim3(kThreads), 0, st, p);
+  void* args[] = {&p};
+  if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
+    return SSIM_ERR_HIP;
   return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
@@ -811,15 +866,17 @@ int ssim_backward(const float* dloss, const float* img1, const float* img2, int6
   p.dloss = dloss;
   p.gx = grad_img1;
   p.gy = grad_img2;
+  p.k_m2 = (float)(-2.0 / ((double)s.planes * (double)s.Ho * (double)s.Wo));
 
   const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % 16 == 0) && ((uintptr_t)img2 % 16 == 0) &&
                    ((uintptr_t)grad_img1 % 16 == 0) && ((uintptr_t)grad_img2 % 16 == 0);
-  const int G = grid_for(d, vec ? 2 : 3, p.units);
+  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
+  const int which = !vec ? kKBwdUnaligned : stream_st ? kKBwdStream : kKBwd;
+  const int G = grid_for(d, which, p.units);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (vec)
-    hipLaunchKernelGGL(ssim_bwd_kernel, dim3(G), dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(ssim_bwd_unaligned_kernel, dim3(G), dim3(kThreads), 0, st, p);
+  void* args[] = {&p};
+  if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
+    return SSIM_ERR_HIP;
   return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 

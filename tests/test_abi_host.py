@@ -54,7 +54,7 @@ def test_map_shape_matches_oracle(H, W, padding):
 
 
 def test_saved_maps_bytes():
-    # four fp32 maps per plane, row pitch = Wo rounded up to 4
+    # four fp32 map planes per image plane, row pitch = Wo rounded up to 4
     assert S.ssim_saved_maps_bytes(1, 3, 1080, 1920, "valid") == 16 * 3 * 1070 * 1912
     assert S.ssim_saved_maps_bytes(1, 3, 1080, 1920, "same") == 16 * 3 * 1080 * 1920
     assert S.ssim_saved_maps_bytes(8, 3, 2160, 3840, "valid") == 16 * 24 * 2150 * 3832
@@ -83,7 +83,7 @@ def test_forward_argument_errors_return_before_any_hip_call():
     assert _fwd(lib, C=-1) == -2
     assert _fwd(lib, H=10) == -2          # valid needs H >= 11
     assert _fwd(lib, W=10) == -2
-    assert _fwd(lib, H=1 << 14, W=1 << 14) == -4   # a plane of 2^28 elements
+    assert _fwd(lib, H=(1 << 14) + 1, W=1 << 13) == -4   # a plane over 2^27 elements
     assert _fwd(lib, H=11, W=(1 << 20) + 1) == -4  # a row longer than 2^20
     assert _fwd(lib, maps=0x300004) == -2          # saved maps must be 16-byte aligned
     assert _fwd(lib, loss=0x1000 + 64) == -5       # loss inside img1
