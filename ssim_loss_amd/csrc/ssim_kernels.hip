@@ -55,13 +55,14 @@
 //                 loss partials from the saved quantities as it reads them:
 //                 the forward is ALU-bound and the backward memory-bound, so
 //                 the partials' arithmetic sits where it is free.
-// Work is split into (plane, strip, output row) units; each workgroup takes
-// an equal contiguous range of units (a persistent-style grid of about one
-// wave of resident workgroups), marching down its strips so that every
-// input row is loaded and column-blurred once per strip, plus a 10-row
-// warm-up where a range starts.  Workgroup ids are remapped so that each of
-// the 8 XCDs (separate L2s) owns one contiguous eighth of the units: strips
-// that share a 10-column halo then run side by side on the same L2.
+// Work is split by strip-column ((plane, strip) pairs): on a grid of about
+// one wave of resident workgroups, each strip-column is cut into equal row
+// ranges, one per workgroup (or, with more strip-columns than workgroups,
+// each workgroup takes whole strip-columns), so every workgroup gets the
+// same work.  A workgroup marches down its range so that every input row is
+// loaded and column-blurred once, plus a 10-row warm-up where the range
+// starts.  Workgroup ids are remapped so that each of the 8 XCDs (separate
+// L2s) owns one contiguous eighth of the grid.
 //
 // Loss reduction: the map entries of 1 - S are summed as per-lane fp32 sums
 // of 4 outputs -> fp64 per lane -> wave64 shuffle tree -> LDS -> one fp64
@@ -142,7 +143,9 @@ struct Params {
   int out_h, out_w;     // output extent (fwd: Ho x Wo, bwd: H x W)
   int off;              // in row = out row + a - off (same for columns)
   int strips;           // ceil(out_w / kStripOut)
-  int64_t units;        // planes * strips * out_h
+  int64_t cols;         // strip-columns: planes * strips
+  int parts;            // > 1: workgroups per strip-column (each takes a row range)
+  int per_block;        // parts == 1: whole strip-columns per workgroup
   // images (fwd: the inputs; bwd: read by the chain rule)
   const float* x;
   const float* y;
@@ -491,24 +494,35 @@ __device__ __forceinline__ void strip_body(const Params& p) {
   // in turn; give each XCD one contiguous eighth of the work.
   int lb = blockIdx.x;
   if ((G & 7) == 0) lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int64_t u_begin = (int64_t)lb * p.units / G;
-  const int64_t u_end = (int64_t)(lb + 1) * p.units / G;
+  // This workgroup's share: one row range of one strip-column, or a run of
+  // whole strip-columns.  Every workgroup gets the same amount of work, so
+  // the grid (one resident wave of workgroups) finishes together.
+  int64_t sc_begin, sc_end;
+  int row_begin, row_end;
+  if (p.parts > 1) {
+    sc_begin = lb / p.parts;
+    sc_end = sc_begin + 1;
+    const int part = lb - (int)sc_begin * p.parts;
+    row_begin = (int)((int64_t)part * p.out_h / p.parts);
+    row_end = (int)((int64_t)(part + 1) * p.out_h / p.parts);
+  } else {
+    sc_begin = (int64_t)lb * p.per_block;
+    sc_end = sc_begin + p.per_block < p.cols ? sc_begin + p.per_block : p.cols;
+    row_begin = 0;
+    row_end = p.out_h;
+  }
 
   float dl = 0.0f;
   if constexpr (MODE == kBwd) dl = *p.dloss;
 
   double acc = 0.0;
   int buf = 0;
-  const int64_t per_plane = (int64_t)p.strips * p.out_h;
-  for (int64_t u = u_begin; u < u_end;) {
+  for (int64_t sc = sc_begin; sc < sc_end; ++sc) {
     Seg<MODE> s;
-    const int64_t plane = u / per_plane;
-    const int64_t rem = u - plane * per_plane;
-    const int strip = (int)(rem / p.out_h);
-    s.row0 = (int)(rem - (int64_t)strip * p.out_h);
-    const int64_t left = u_end - u;
-    s.nrows = (int)((int64_t)(p.out_h - s.row0) < left ? (int64_t)(p.out_h - s.row0) : left);
-    u += s.nrows;
+    const int64_t plane = sc / p.strips;
+    const int strip = (int)(sc - plane * p.strips);
+    s.row0 = row_begin;
+    s.nrows = row_end - row_begin;
     s.j0 = strip * kStripOut;
     const int c = s.j0 - p.off + tid;  // this lane's input column
     s.colbyte = (c >= 0 && c < p.in_w) ? (unsigned)c * 4u : kOob;
@@ -713,14 +727,26 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, Shape* 
   return SSIM_OK;
 }
 
-int grid_for(const DeviceInfo* d, int which, int64_t units) {
-  int64_t g = (units + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
-  const int64_t resident = (int64_t)d->cus * d->occ[which];
-  if (g > resident) g = resident;
-  if (g > kMaxBlocks) g = kMaxBlocks;
-  if (g >= 8) g &= ~(int64_t)7;
-  if (g < 1) g = 1;
-  return (int)g;
+// Grid: one resident wave of workgroups (CUs x occupancy), or fewer when
+// the work is small.  With fewer strip-columns than resident workgroups,
+// each strip-column is split into `parts` equal row ranges of at least
+// kMinRowsPerBlock rows; otherwise each workgroup takes `per_block` whole
+// strip-columns.
+int plan_grid(const DeviceInfo* d, int which, Params& p) {
+  int64_t resident = (int64_t)d->cus * d->occ[which];
+  if (resident > kMaxBlocks) resident = kMaxBlocks;
+  if (p.cols >= resident) {
+    p.parts = 1;
+    p.per_block = (int)((p.cols + resident - 1) / resident);
+    return (int)((p.cols + p.per_block - 1) / p.per_block);
+  }
+  int64_t parts = resident / p.cols;
+  const int64_t max_parts = (p.out_h + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
+  if (parts > max_parts) parts = max_parts;
+  if (parts < 1) parts = 1;
+  p.parts = (int)parts;
+  p.per_block = 1;
+  return (int)(p.cols * parts);
 }
 
 void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane, int out_h,
@@ -733,7 +759,7 @@ void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane
   p.out_w = out_w;
   p.off = off;
   p.strips = (out_w + kStripOut - 1) / kStripOut;
-  p.units = planes * p.strips * (int64_t)out_h;
+  p.cols = planes * p.strips;
 }
 
 }  // namespace
@@ -822,7 +848,7 @@ int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int
 
   const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
   const int which = !saved_maps ? kKFwdInfer : stream_st ? kKFwdTrainStream : kKFwdTrain;
-  const int G = grid_for(d, which, p.units);
+  const int G = plan_grid(d, which, p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
   if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
@@ -872,7 +898,7 @@ int ssim_backward(const float* dloss, const float* img1, const float* img2, int6
                    ((uintptr_t)grad_img1 % 16 == 0) && ((uintptr_t)grad_img2 % 16 == 0);
   const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
   const int which = !vec ? kKBwdUnaligned : stream_st ? kKBwdStream : kKBwd;
-  const int G = grid_for(d, which, p.units);
+  const int G = plan_grid(d, which, p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
   if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
