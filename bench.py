@@ -5,6 +5,7 @@ ssim_backward (both image gradients) on one batch of synthetic images already
 resident in HBM, through the C ABI on torch's current stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--dtype float32|float16|bfloat16]
 
 Prints one JSON line: metric Mpix/s (pixels = N*H*W per step, wall clock over
 K steps), the roofline of the dominant kernel (algorithmic bytes per launch /
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PAGES_MPIX_S = 1920 * 1080 / 7.2e-3 / 1e6  # the pages' 7.2 ms fwd+bwd at 1080p (RDNA4 R9700)
-KERNEL_SRC = os.path.join(ROOT, "ssim_loss_amd", "csrc", "ssim_kernels.hip")
+CSRC = os.path.join(ROOT, "ssim_loss_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -36,6 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="1080p-valid")
+    ap.add_argument("--dtype", default="float32", choices=["float32", "float16", "bfloat16"],
+                    help="storage type of images and gradients (arithmetic is fp32)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with a cache flush before each (0 = skip)")
@@ -45,20 +48,27 @@ def parse():
 
 
 def source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the library's sources (every file under csrc/, in name order)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(shape, padding):
-    """Compulsory HBM bytes per launch of each kernel (saved-maps design):
-    forward reads x, y (8 B per input element) and writes four fp32 maps
-    (16 B per map entry); backward reads the maps (16 B per entry), x and y
-    (8 B per element) and writes both gradients (8 B per element)."""
+def algorithmic_bytes(shape, padding, eb=4):
+    """Compulsory HBM bytes per launch of each kernel (saved-maps design), for
+    images and gradients of eb bytes per element: forward reads x, y (2 eb per
+    input element) and writes four fp32 maps (16 B per map entry); backward
+    reads the maps (16 B per entry), x and y (2 eb per element) and writes
+    both gradients (2 eb per element)."""
     N, C, H, W = shape
     Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
     e_in = N * C * H * W
     e_out = N * C * Ho * Wo
-    return {"ssim_forward": 8 * e_in + 16 * e_out, "ssim_backward": 16 * e_out + 16 * e_in}
+    return {"ssim_forward": 2 * eb * e_in + 16 * e_out,
+            "ssim_backward": 16 * e_out + 4 * eb * e_in,
+            "ssim_forward(inference)": 2 * eb * e_in}
 
 
 def cpu_baseline(x, y, padding, pixels_per_image_batch):
@@ -108,8 +118,10 @@ def main():
     N, C, H, W = x.shape
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t1 = torch.from_numpy(x).to(dev)
-    t2 = torch.from_numpy(y).to(dev)
+    tdtype = getattr(torch, args.dtype)
+    eb = torch.empty((), dtype=tdtype).element_size()
+    t1 = torch.from_numpy(x).to(dev).to(tdtype).contiguous()
+    t2 = torch.from_numpy(y).to(dev).to(tdtype).contiguous()
     loss = torch.empty((), dtype=torch.float32, device=dev)
     maps = S.alloc_saved_maps(t1, w.padding)
     ws = S.workspace_for(dev)
@@ -151,6 +163,8 @@ def main():
 
     fwd_ms = per_launch_ms(lambda: S.ssim_forward(t1, t2, w.padding, loss, maps, ws))
     bwd_ms = per_launch_ms(lambda: S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2))
+    # inference forward: the loss only, nothing saved for a backward
+    inf_ms = per_launch_ms(lambda: S.ssim_forward(t1, t2, w.padding, loss, None, ws))
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
@@ -180,7 +194,7 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    alg = algorithmic_bytes((N, C, H, W), w.padding)
+    alg = algorithmic_bytes((N, C, H, W), w.padding, eb)
     kern = {"ssim_forward": fwd_ms, "ssim_backward": bwd_ms}
     dom = max(kern, key=kern.get)
     achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
@@ -189,11 +203,13 @@ def main():
     # WRITE_SIZE, scaled by a copy kernel of known size), valid only for the
     # kernel source they were taken from
     traffic = None
-    traffic_file = os.path.join(PROFILES, f"hbm_traffic_{args.workload}.json")
+    tag = args.workload if args.dtype == "float32" else f"{args.workload}-{args.dtype}"
+    traffic_file = os.path.join(PROFILES, f"hbm_traffic_{tag}.json")
     if os.path.exists(traffic_file):
         with open(traffic_file) as f:
             tr = json.load(f)
         if (tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload
+                and tr.get("dtype", "float32") == args.dtype
                 and dom in tr.get("bytes_per_launch", {})):
             traffic = tr["bytes_per_launch"][dom]
 
@@ -207,8 +223,10 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_MPIX_S, 2) if args.workload == "1080p-valid" else None,
-        "dtype": "f32",
+        "vs_baseline": (round(value / PAGES_MPIX_S, 2)
+                        if args.workload == "1080p-valid" and args.dtype == "float32" else None),
+        "dtype": {"float32": "f32", "float16": "f16 I/O, f32 math",
+                  "bfloat16": "bf16 I/O, f32 math"}[args.dtype],
         "data": "synthetic",
         "config": {"workload": args.workload, "shape": [N, C, H, W], "padding": w.padding},
         "roofline": {
@@ -221,7 +239,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": alg[dom],
         },
-        "kernels_ms": {"ssim_forward": round(fwd_ms, 5), "ssim_backward": round(bwd_ms, 5)},
+        "kernels_ms": {"ssim_forward": round(fwd_ms, 5), "ssim_backward": round(bwd_ms, 5),
+                       "ssim_forward(inference)": round(inf_ms, 5)},
+        "inference": {"mpix_per_s": round(mpix / (inf_ms * 1e-3), 1),
+                      "hbm_gbs": round(alg["ssim_forward(inference)"] / (inf_ms * 1e-3) / 1e9, 1)},
         "step_hbm_gbs": round((alg["ssim_forward"] + alg["ssim_backward"]) /
                               ((fwd_ms + bwd_ms) * 1e-3) / 1e9, 1),
         "cold": cold,

@@ -18,8 +18,10 @@
  *     memory) owned by the caller.  The library never allocates, frees or
  *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) and completes asynchronously.
- *   - Images are contiguous fp32 NCHW, N*C planes of H rows of W pixels.
- *     img1 and img2 have the same shape.  Values are meant to lie in [0,1].
+ *   - Images are contiguous NCHW (fp32 for ssim_forward / ssim_backward,
+ *     fp32, fp16 or bf16 for the _typed calls), N*C planes of H rows of W
+ *     pixels, each pointer aligned to its element size.  img1 and img2 have
+ *     the same shape.  Values are meant to lie in [0,1].
  *   - Outputs are overwritten, never accumulated into.
  *   - Every argument check happens before any HIP call; a failed check
  *     returns a negative code and enqueues nothing.  A launch failure
@@ -38,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 1
+#define SSIM_ABI_VERSION 2
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -50,13 +52,24 @@ enum {
 enum {
   SSIM_OK = 0,
   SSIM_ERR_NULL = -1,     /* a required pointer is NULL */
-  SSIM_ERR_SHAPE = -2,    /* N, C, H or W <= 0, or valid padding with H < 11 or W < 11 */
+  SSIM_ERR_SHAPE = -2,    /* N, C, H or W <= 0, valid padding with H < 11 or W < 11, an
+                             image or gradient pointer not aligned to its element size,
+                             or saved_maps not 16-byte aligned */
   SSIM_ERR_PADDING = -3,  /* padding is neither SSIM_PAD_VALID nor SSIM_PAD_SAME */
   SSIM_ERR_OVERFLOW = -4, /* a plane (image, or map with its row pitch) holds more than
                              2^27 elements, a row more than 2^20, or a size overflows */
   SSIM_ERR_ALIAS = -5,    /* an output buffer overlaps an input or another output */
   SSIM_ERR_HIP = -6,      /* a HIP runtime call failed (launch, device query) */
-  SSIM_ERR_DEVICE = -7    /* the current device is not a wave64 gfx9 GPU */
+  SSIM_ERR_DEVICE = -7,   /* the current device is not a wave64 gfx950 GPU */
+  SSIM_ERR_DTYPE = -8     /* dtype is not one of SSIM_DTYPE_* */
+};
+
+/* storage type of images and gradients for the _typed entry points; the
+ * arithmetic is fp32 in every case and the saved maps are always fp32 */
+enum {
+  SSIM_DTYPE_F32 = 0,
+  SSIM_DTYPE_F16 = 1, /* IEEE binary16 */
+  SSIM_DTYPE_BF16 = 2 /* bfloat16 (the top 16 bits of an fp32); gradients rounded to nearest even */
 };
 
 /* Version of this ABI (SSIM_ABI_VERSION of the library that was built). */
@@ -129,6 +142,20 @@ int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int
 int ssim_backward(const float* dloss, const float* img1, const float* img2, int64_t N,
                   int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
                   float* grad_img1, float* grad_img2, void* stream);
+
+/* Half-precision image I/O: ssim_forward / ssim_backward for images (and
+ * gradients) stored as `dtype` (SSIM_DTYPE_F32, _F16 or _BF16), same shape
+ * and layout rules, all arithmetic in fp32 and maps in fp32.  Elements are
+ * widened exactly on load; gradients are rounded to nearest even on store.
+ * fp32 calls behave exactly as ssim_forward / ssim_backward.  Halving the
+ * image and gradient bytes is the point: a training step moves 44 bytes per
+ * element instead of 56.  Returns SSIM_ERR_DTYPE for an unknown dtype. */
+int ssim_forward_typed(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
+                       int64_t H, int64_t W, int padding, float* loss, float* saved_maps,
+                       void* workspace, void* stream);
+int ssim_backward_typed(const float* dloss, const void* img1, const void* img2, int dtype,
+                        int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                        const float* saved_maps, void* grad_img1, void* grad_img2, void* stream);
 
 #ifdef __cplusplus
 }

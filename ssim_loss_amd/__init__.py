@@ -6,7 +6,9 @@ current HIP stream.  Every step of the computation runs in the HIP kernels of
 ``libssim_loss_amd.so``; there is no fallback path.  If the library is
 missing, importing the functions below raises.
 
-Functions with the C names:
+Functions with the C names (images and gradients may be float32, float16 or
+bfloat16 tensors; the C functions ssim_forward_typed / ssim_backward_typed
+are called for the half types):
   ssim_forward(img1, img2, padding, loss, saved_maps, workspace)
   ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2)
   ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
@@ -25,6 +27,7 @@ from .build import LIB_PATH
 
 PAD = {"valid": 0, "same": 1}
 SSIM_OK = 0
+SSIM_DTYPE = {"float32": 0, "float16": 1, "bfloat16": 2}
 
 _lib = None
 _lock = threading.Lock()
@@ -66,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.ssim_forward.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp, vp, vp]
         L.ssim_backward.restype = i32
         L.ssim_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp, vp, vp, vp]
+        L.ssim_forward_typed.restype = i32
+        L.ssim_forward_typed.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp]
+        L.ssim_backward_typed.restype = i32
+        L.ssim_backward_typed.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp,
+                                          vp]
         _lib = L
     return _lib
 
@@ -120,13 +128,17 @@ def _dptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _dtype_code(t) -> int:
+    return SSIM_DTYPE[str(t.dtype).replace("torch.", "")]
+
+
 def _check_image(t, name):
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise TypeError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
     if t.device.type != "cuda":
         raise TypeError(f"{name} must be a GPU tensor, got device {t.device}")
     if t.dim() != 4:
@@ -142,9 +154,17 @@ def ssim_forward(img1, img2, padding, loss, saved_maps, workspace) -> None:
     _check_image(img2, "img2")
     if img1.shape != img2.shape:
         raise ValueError("img1 and img2 must have the same shape")
+    if img1.dtype != img2.dtype:
+        raise TypeError("img1 and img2 must have the same dtype")
     N, C, H, W = img1.shape
-    rc = lib().ssim_forward(_dptr(img1), _dptr(img2), N, C, H, W, _pad(padding), _dptr(loss),
-                            _dptr(saved_maps), _dptr(workspace), _stream_ptr(img1))
+    code = _dtype_code(img1)
+    if code == 0:
+        rc = lib().ssim_forward(_dptr(img1), _dptr(img2), N, C, H, W, _pad(padding), _dptr(loss),
+                                _dptr(saved_maps), _dptr(workspace), _stream_ptr(img1))
+    else:
+        rc = lib().ssim_forward_typed(_dptr(img1), _dptr(img2), code, N, C, H, W, _pad(padding),
+                                      _dptr(loss), _dptr(saved_maps), _dptr(workspace),
+                                      _stream_ptr(img1))
     if rc != SSIM_OK:
         raise SsimError(rc, "ssim_forward")
 
@@ -153,10 +173,21 @@ def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) 
     """Calls the C ``ssim_backward`` on torch's current stream."""
     _check_image(img1, "img1")
     _check_image(img2, "img2")
+    if img1.dtype != img2.dtype:
+        raise TypeError("img1 and img2 must have the same dtype")
+    for g in (grad_img1, grad_img2):
+        if g is not None and (g.dtype != img1.dtype or g.shape != img1.shape):
+            raise TypeError("gradients must have the images' dtype and shape")
     N, C, H, W = img1.shape
-    rc = lib().ssim_backward(_dptr(dloss), _dptr(img1), _dptr(img2), N, C, H, W, _pad(padding),
-                             _dptr(saved_maps), _dptr(grad_img1), _dptr(grad_img2),
-                             _stream_ptr(img1))
+    code = _dtype_code(img1)
+    if code == 0:
+        rc = lib().ssim_backward(_dptr(dloss), _dptr(img1), _dptr(img2), N, C, H, W,
+                                 _pad(padding), _dptr(saved_maps), _dptr(grad_img1),
+                                 _dptr(grad_img2), _stream_ptr(img1))
+    else:
+        rc = lib().ssim_backward_typed(_dptr(dloss), _dptr(img1), _dptr(img2), code, N, C, H, W,
+                                       _pad(padding), _dptr(saved_maps), _dptr(grad_img1),
+                                       _dptr(grad_img2), _stream_ptr(img1))
     if rc != SSIM_OK:
         raise SsimError(rc, "ssim_backward")
 
@@ -234,6 +265,8 @@ def ssim_loss(img1, img2, padding: str = "valid", train: bool = True):
     _check_image(img2, "img2")
     if img1.shape != img2.shape:
         raise ValueError("img1 and img2 must have the same shape")
+    if img1.dtype != img2.dtype:
+        raise TypeError("img1 and img2 must have the same dtype")
     _pad(padding)
     return _fn.apply(img1, img2, padding, bool(train))
 

@@ -1,19 +1,25 @@
-"""Build step for the HIP library: one ``hipcc`` call producing
-``ssim_loss_amd/libssim_loss_amd.so`` for gfx950.
+"""Build step for the HIP library: the translation units under csrc/ are
+compiled in parallel with ``hipcc`` for gfx950 and linked into
+``ssim_loss_amd/libssim_loss_amd.so``.
 
 Packed-FP32 instructions are switched off (``-packed-fp32-ops``); the kernels
 are written so that nothing depends on them.
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "ssim_kernels.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+HEADERS = sorted(glob.glob(os.path.join(CSRC, "*.hpp")))
 INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libssim_loss_amd.so")
 ARCH = "gfx950"
 
@@ -25,16 +31,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def compile_cmd(out: str, extra: list[str] | None = None) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-I", INCLUDE,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            *(extra or []), "-o", out, SRC]
+def compile_flags(extra: list[str] | None = None) -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE,
+            "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            *(extra or [])]
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        cmd = [cc, *compile_flags(extra), "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = compile_cmd(tmp, extra)
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,336 @@
+// ssim_api.hip -- host side of the fused SSIM loss: the C ABI declared in
+// ssim_loss_amd.h, argument checks (all before any HIP call), per-device
+// launch planning and the launches.  The kernels live in ssim_device.hpp and
+// are instantiated per image type in ssim_kernels_{f32,f16,bf16}.hip.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "ssim_device.hpp"
+#include "ssim_loss_amd.h"
+
+namespace {
+
+using namespace ssim_dev;
+
+constexpr int kTypes = 3;  // SSIM_DTYPE_F32, SSIM_DTYPE_F16, SSIM_DTYPE_BF16
+
+const void* const* kernel_table(int dtype) {
+  switch (dtype) {
+    case SSIM_DTYPE_F16: return ssim_kernel_table_f16();
+    case SSIM_DTYPE_BF16: return ssim_kernel_table_bf16();
+    default: return ssim_kernel_table_f32();
+  }
+}
+
+// Bytes a training step touches in HBM (both images, the saved maps, both
+// gradients).  Above this the step cannot stay in the 256 MB last-level
+// cache between the forward and the backward, and the stores stream
+// (non-temporal); below it they stay cacheable so that the backward finds
+// the maps there.
+constexpr size_t kStreamBytes = (size_t)256 << 20;
+
+struct DeviceInfo {
+  bool ready = false;
+  int status = SSIM_OK;
+  int cus = 0;
+  int occ[kTypes][kKinds] = {};  // resident workgroups per CU, per entry kernel
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+int device_info(const DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSIM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSIM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SSIM_ERR_HIP;
+    if (prop.warpSize != kWave || strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      d.status = SSIM_ERR_DEVICE;
+    } else {
+      d.cus = prop.multiProcessorCount;
+      for (int t = 0; t < kTypes; ++t)
+        for (int k = 0; k < kKinds; ++k) {
+          int n = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_table(t)[k], kThreads, 0) !=
+              hipSuccess)
+            return SSIM_ERR_HIP;
+          d.occ[t][k] = n > 0 ? n : 1;
+        }
+      d.status = SSIM_OK;
+    }
+    d.ready = true;
+  }
+  *out = &d;
+  return d.status;
+}
+
+int64_t roundup4(int64_t v) { return (v + 3) & ~(int64_t)3; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int elem_bytes(int dtype) { return dtype == SSIM_DTYPE_F32 ? 4 : 2; }
+// an image or gradient pointer must be aligned to its element size
+bool misaligned(const void* ptr, int dtype) {
+  return ((uintptr_t)ptr % (uintptr_t)elem_bytes(dtype)) != 0;
+}
+
+struct Shape {
+  int64_t N, C, H, W, Ho, Wo, pitch, planes;
+  size_t img_bytes, map_bytes;
+};
+
+int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, int dtype, Shape* s) {
+  if (padding != SSIM_PAD_VALID && padding != SSIM_PAD_SAME) return SSIM_ERR_PADDING;
+  if (dtype != SSIM_DTYPE_F32 && dtype != SSIM_DTYPE_F16 && dtype != SSIM_DTYPE_BF16)
+    return SSIM_ERR_DTYPE;
+  if (N <= 0 || C <= 0 || H <= 0 || W <= 0) return SSIM_ERR_SHAPE;
+  const int64_t Ho = padding == SSIM_PAD_VALID ? H - 10 : H;
+  const int64_t Wo = padding == SSIM_PAD_VALID ? W - 10 : W;
+  if (Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
+  // Buffer offsets are 32-bit: a plane (image, or map with its row pitch)
+  // holds at most 2^27 elements and a row at most 2^20, so valid offsets
+  // stay below 2^29 and the out-of-range ones (rows above the plane wrap to
+  // just below 2^32; the 2^31 marker plus at most 14 rows of 4 MiB) stay
+  // above 2^30.
+  const int64_t lim = (int64_t)1 << 27;
+  if (W > ((int64_t)1 << 20) || H > lim / W) return SSIM_ERR_OVERFLOW;
+  const int64_t pitch = roundup4(Wo);
+  if (H * W > lim || Ho * pitch > lim) return SSIM_ERR_OVERFLOW;
+  if (N > (int64_t)1 << 40 || C > ((int64_t)1 << 40) / N) return SSIM_ERR_OVERFLOW;
+  const int64_t planes = N * C;
+  // bytes must fit comfortably in 64 bits
+  if (planes > ((int64_t)1 << 58) / (H * W) || planes > ((int64_t)1 << 56) / (Ho * pitch))
+    return SSIM_ERR_OVERFLOW;
+  s->N = N; s->C = C; s->H = H; s->W = W; s->Ho = Ho; s->Wo = Wo; s->pitch = pitch;
+  s->planes = planes;
+  s->img_bytes = (size_t)(planes * H * W) * elem_bytes(dtype);
+  s->map_bytes = (size_t)(planes * Ho * pitch) * 4 * sizeof(float);
+  return SSIM_OK;
+}
+
+// Grid: one resident wave of workgroups (CUs x occupancy), or fewer when
+// the work is small.  With fewer strip-columns than resident workgroups,
+// each strip-column is split into `parts` equal row ranges of at least
+// kMinRowsPerBlock rows; otherwise each workgroup takes `per_block` whole
+// strip-columns.
+int plan_grid(const DeviceInfo* d, int dtype, int which, Params& p) {
+  int64_t resident = (int64_t)d->cus * d->occ[dtype][which];
+  if (resident > kMaxBlocks) resident = kMaxBlocks;
+  if (p.cols >= resident) {
+    p.parts = 1;
+    p.per_block = (int)((p.cols + resident - 1) / resident);
+    return (int)((p.cols + p.per_block - 1) / p.per_block);
+  }
+  int64_t parts = resident / p.cols;
+  const int64_t max_parts = (p.out_h + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
+  if (parts > max_parts) parts = max_parts;
+  if (parts < 1) parts = 1;
+  p.parts = (int)parts;
+  p.per_block = 1;
+  return (int)(p.cols * parts);
+}
+
+void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane, int out_h,
+                   int out_w, int off, int64_t planes) {
+  p.in_h = in_h;
+  p.in_w = in_w;
+  p.in_pitch = in_pitch;
+  p.in_plane = in_plane;
+  p.out_h = out_h;
+  p.out_w = out_w;
+  p.off = off;
+  p.strips = (out_w + kStripOut - 1) / kStripOut;
+  p.cols = planes * p.strips;
+}
+
+int launch(const DeviceInfo* d, int dtype, int which, Params& p, void* stream) {
+  const int G = plan_grid(d, dtype, which, p);
+  void* args[] = {&p};
+  if (hipLaunchKernel(kernel_table(dtype)[which], dim3(G), dim3(kThreads), args, 0,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSIM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
+}
+
+int forward_impl(const void* img1, const void* img2, int dtype, int64_t N, int64_t C, int64_t H,
+                 int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
+                 void* stream) {
+  if (!img1 || !img2 || !loss || !workspace) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if (saved_maps && ((uintptr_t)saved_maps & 15u)) return SSIM_ERR_SHAPE;
+  if (misaligned(img1, dtype) || misaligned(img2, dtype)) return SSIM_ERR_SHAPE;
+  const size_t wsb = sizeof(Workspace);
+  const void* outs[3] = {loss, saved_maps, workspace};
+  const size_t outb[3] = {sizeof(float), saved_maps ? s.map_bytes : 0, wsb};
+  for (int k = 0; k < 3; ++k) {
+    if (overlaps(outs[k], outb[k], img1, s.img_bytes) || overlaps(outs[k], outb[k], img2, s.img_bytes))
+      return SSIM_ERR_ALIAS;
+    for (int l = k + 1; l < 3; ++l)
+      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
+  }
+
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  const int off = padding == SSIM_PAD_VALID ? 0 : 5;
+  fill_geometry(p, (int)s.H, (int)s.W, (int)s.W, s.H * s.W, (int)s.Ho, (int)s.Wo, off, s.planes);
+  p.x = img1;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.maps = saved_maps;
+  p.map_pitch = (int)s.pitch;
+  p.map_plane = s.Ho * s.pitch;
+  const double M = (double)s.planes * (double)s.Ho * (double)s.Wo;
+  p.k_m2 = (float)(-2.0 / M);
+  p.inv_m = 1.0 / M;
+  p.loss = loss;
+  p.ws = static_cast<Workspace*>(workspace);
+
+  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
+  const int which = !saved_maps ? kKFwdInfer : stream_st ? kKFwdTrainStream : kKFwdTrain;
+  return launch(d, dtype, which, p, stream);
+}
+
+int backward_impl(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
+                  int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
+                  void* grad_img1, void* grad_img2, void* stream) {
+  if (!dloss || !img1 || !img2 || !saved_maps) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if ((uintptr_t)saved_maps & 15u) return SSIM_ERR_SHAPE;
+  if (misaligned(img1, dtype) || misaligned(img2, dtype) || misaligned(grad_img1, dtype) ||
+      misaligned(grad_img2, dtype))
+    return SSIM_ERR_SHAPE;
+  const void* ins[4] = {dloss, img1, img2, saved_maps};
+  const size_t inb[4] = {sizeof(float), s.img_bytes, s.img_bytes, s.map_bytes};
+  void* outs[2] = {grad_img1, grad_img2};
+  for (int k = 0; k < 2; ++k)
+    for (int l = 0; l < 4; ++l)
+      if (overlaps(outs[k], s.img_bytes, ins[l], inb[l])) return SSIM_ERR_ALIAS;
+  if (overlaps(grad_img1, s.img_bytes, grad_img2, s.img_bytes)) return SSIM_ERR_ALIAS;
+  if (!grad_img1 && !grad_img2) return SSIM_OK;
+
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  const int off = padding == SSIM_PAD_VALID ? 10 : 5;
+  fill_geometry(p, (int)s.Ho, (int)s.Wo, (int)s.pitch, s.Ho * s.pitch * 4, (int)s.H, (int)s.W,
+                off, s.planes);
+  p.x = img1;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.maps = const_cast<float*>(saved_maps);
+  p.map_pitch = (int)s.pitch;
+  p.map_plane = s.Ho * s.pitch;
+  p.dloss = dloss;
+  p.gx = grad_img1;
+  p.gy = grad_img2;
+  p.k_m2 = (float)(-2.0 / ((double)s.planes * (double)s.Ho * (double)s.Wo));
+
+  // 4-wide groups of image elements: 16 bytes (fp32) or 8 bytes (fp16, bf16)
+  const uintptr_t al = (uintptr_t)(4 * elem_bytes(dtype));
+  const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % al == 0) && ((uintptr_t)img2 % al == 0) &&
+                   ((uintptr_t)grad_img1 % al == 0) && ((uintptr_t)grad_img2 % al == 0);
+  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
+  const int which = !vec ? kKBwdUnaligned : stream_st ? kKBwdStream : kKBwd;
+  return launch(d, dtype, which, p, stream);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int ssim_abi_version(void) { return SSIM_ABI_VERSION; }
+
+const char* ssim_strerror(int code) {
+  switch (code) {
+    case SSIM_OK: return "success";
+    case SSIM_ERR_NULL: return "a required pointer is NULL";
+    case SSIM_ERR_SHAPE: return "bad shape: N, C, H, W must be positive and valid padding needs H, W >= 11";
+    case SSIM_ERR_PADDING: return "padding must be SSIM_PAD_VALID (0) or SSIM_PAD_SAME (1)";
+    case SSIM_ERR_OVERFLOW: return "a plane holds more than 2^27 elements, a row more than 2^20, or a size overflows";
+    case SSIM_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case SSIM_ERR_HIP: return "a HIP runtime call failed";
+    case SSIM_ERR_DEVICE: return "the current device is not a wave64 gfx950 GPU";
+    case SSIM_ERR_DTYPE: return "dtype must be SSIM_DTYPE_F32 (0), SSIM_DTYPE_F16 (1) or SSIM_DTYPE_BF16 (2)";
+    default: return "unknown error code";
+  }
+}
+
+void ssim_taps(float out[11]) {
+  for (int k = 0; k < 11; ++k) out[k] = tap(k);
+}
+
+int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo) {
+  if (!Ho || !Wo) return SSIM_ERR_NULL;
+  Shape s;
+  const int rc = check_shape(1, 1, H, W, padding, SSIM_DTYPE_F32, &s);
+  if (rc != SSIM_OK) return rc;
+  *Ho = s.Ho;
+  *Wo = s.Wo;
+  return SSIM_OK;
+}
+
+size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding) {
+  Shape s;
+  if (check_shape(N, C, H, W, padding, SSIM_DTYPE_F32, &s) != SSIM_OK) return 0;
+  return s.map_bytes;
+}
+
+size_t ssim_workspace_bytes(void) { return sizeof(Workspace); }
+
+int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int64_t H,
+                 int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
+                 void* stream) {
+  return forward_impl(img1, img2, SSIM_DTYPE_F32, N, C, H, W, padding, loss, saved_maps,
+                      workspace, stream);
+}
+
+int ssim_backward(const float* dloss, const float* img1, const float* img2, int64_t N,
+                  int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
+                  float* grad_img1, float* grad_img2, void* stream) {
+  return backward_impl(dloss, img1, img2, SSIM_DTYPE_F32, N, C, H, W, padding, saved_maps,
+                       grad_img1, grad_img2, stream);
+}
+
+int ssim_forward_typed(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
+                       int64_t H, int64_t W, int padding, float* loss, float* saved_maps,
+                       void* workspace, void* stream) {
+  return forward_impl(img1, img2, dtype, N, C, H, W, padding, loss, saved_maps, workspace, stream);
+}
+
+int ssim_backward_typed(const float* dloss, const void* img1, const void* img2, int dtype,
+                        int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                        const float* saved_maps, void* grad_img1, void* grad_img2, void* stream) {
+  return backward_impl(dloss, img1, img2, dtype, N, C, H, W, padding, saved_maps, grad_img1,
+                       grad_img2, stream);
+}
+
+}  // extern "C"

@@ -1,4 +1,8 @@
-// ssim_kernels.hip -- fused SSIM loss, forward and backward, for gfx950.
+// ssim_device.hpp -- device side of the fused SSIM loss (forward and
+// backward) for gfx950: constants, kernel parameters and the strip-marching
+// skeleton, templated on direction, store policy and image storage type.
+// Each ssim_kernels_<type>.hip instantiates the entry kernels for one image
+// type; ssim_api.hip is the host side (C ABI, argument checks, launches).
 //
 // What is computed ("Fully Fused Differentiable SSIM", opening section and
 // Usage; "TriSSIM", How it works and Usage): the SSIM map of the 11x11
@@ -70,13 +74,10 @@
 // partials in a fixed order and writes loss = sum / M.  Deterministic; no
 // atomics on floating point.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <string.h>
-
-#include <mutex>
-
-#include "ssim_loss_amd.h"
 
 #if defined(__HIP_DEVICE_COMPILE__)
 #if !defined(__gfx950__)
@@ -84,7 +85,7 @@
 #endif
 #endif
 
-namespace {
+namespace ssim_dev {
 
 constexpr int kWave = 64;        // gfx9 wavefront size; checked on the host at run time
 constexpr int kThreads = 256;    // 4 waves per workgroup
@@ -135,6 +136,14 @@ struct Workspace {
 
 enum Mode { kFwdInfer = 0, kFwdTrain = 1, kBwd = 2 };
 
+// Storage type of images and gradients (the arithmetic is fp32 throughout;
+// maps are always fp32).
+enum ImgType { kImgF32 = 0, kImgF16 = 1, kImgBF16 = 2 };
+template <int T>
+constexpr unsigned img_bytes() {
+  return T == kImgF32 ? 4u : 2u;
+}
+
 struct Params {
   // blur geometry
   int in_h, in_w;       // extent of the blurred input (fwd: H x W, bwd: Ho x Wo)
@@ -146,9 +155,10 @@ struct Params {
   int64_t cols;         // strip-columns: planes * strips
   int parts;            // > 1: workgroups per strip-column (each takes a row range)
   int per_block;        // parts == 1: whole strip-columns per workgroup
-  // images (fwd: the inputs; bwd: read by the chain rule)
-  const float* x;
-  const float* y;
+  // images (fwd: the inputs; bwd: read by the chain rule), of the kernel's
+  // image type
+  const void* x;
+  const void* y;
   int64_t img_plane;    // H * W
   int img_w;            // W
   // maps (fwd: written in training mode; bwd: the blurred input)
@@ -162,8 +172,8 @@ struct Params {
   Workspace* ws;
   // backward
   const float* dloss;
-  float* gx;
-  float* gy;
+  void* gx;             // of the kernel's image type
+  void* gy;
 };
 
 // ---------------------------------------------------------------------------
@@ -184,8 +194,11 @@ using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr unsigned kOob = 0x80000000u;         // offset that is out of range for every plane
 constexpr int kRsrcFlags = 0x00020000;          // gfx9 dword3: 32-bit data format, raw access
 
-__device__ __forceinline__ rsrc_t make_rsrc(const float* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kRsrcFlags);
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+__device__ __forceinline__ const char* byte_ptr(const void* p, int64_t bytes) {
+  return static_cast<const char*>(p) + bytes;
 }
 __device__ __forceinline__ float ld1(rsrc_t r, unsigned off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
@@ -204,6 +217,65 @@ template <bool kNt>
 __device__ __forceinline__ void st4(rsrc_t r, unsigned off, float4 v) {
   using u4 = unsigned __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kNt ? kPolicyNt : 0);
+}
+
+// Image elements: fp32, fp16 or bf16 in memory, fp32 in registers.  bf16 is
+// the top half of an fp32; fp32 -> bf16 rounds to nearest even.
+template <int T>
+__device__ __forceinline__ float half_bits_to_float(unsigned h) {
+  if constexpr (T == kImgF16) return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+  else return __builtin_bit_cast(float, h << 16);
+}
+template <int T>
+__device__ __forceinline__ unsigned float_to_half_bits(float v) {
+  if constexpr (T == kImgF16) {
+    return __builtin_bit_cast(unsigned short, (_Float16)v);
+  } else {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  }
+}
+// one element at byte offset off
+template <int T>
+__device__ __forceinline__ float ld_img(rsrc_t r, unsigned off) {
+  if constexpr (T == kImgF32) return ld1(r, off);
+  else return half_bits_to_float<T>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+// four consecutive elements at byte offset off (aligned to 4 elements)
+template <int T>
+__device__ __forceinline__ void ld_img4(rsrc_t r, unsigned off, float (&v)[4]) {
+  if constexpr (T == kImgF32) {
+    const float4 a = ld4(r, off);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else {
+    using u2 = unsigned __attribute__((ext_vector_type(2)));
+    const u2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v[0] = half_bits_to_float<T>(w.x & 0xffffu);
+    v[1] = half_bits_to_float<T>(w.x >> 16);
+    v[2] = half_bits_to_float<T>(w.y & 0xffffu);
+    v[3] = half_bits_to_float<T>(w.y >> 16);
+  }
+}
+template <int T, bool kNt>
+__device__ __forceinline__ void st_img(rsrc_t r, unsigned off, float v) {
+  if constexpr (T == kImgF32) {
+    st1<kNt>(r, off, v);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)float_to_half_bits<T>(v), r, off, 0,
+                                          kNt ? kPolicyNt : 0);
+  }
+}
+template <int T, bool kNt>
+__device__ __forceinline__ void st_img4(rsrc_t r, unsigned off, const float (&v)[4]) {
+  if constexpr (T == kImgF32) {
+    st4<kNt>(r, off, make_float4(v[0], v[1], v[2], v[3]));
+  } else {
+    using u2 = unsigned __attribute__((ext_vector_type(2)));
+    u2 w;
+    w.x = float_to_half_bits<T>(v[0]) | (float_to_half_bits<T>(v[1]) << 16);
+    w.y = float_to_half_bits<T>(v[2]) | (float_to_half_bits<T>(v[3]) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNt ? kPolicyNt : 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -288,7 +360,7 @@ struct Raw {
 };
 
 // This lane's input pixel(s) in input row r; 0 outside the input extent.
-template <int MODE>
+template <int MODE, int T>
 __device__ __forceinline__ void load_row(const Params& p, const Seg<MODE>& s, int r,
                                          Raw<MODE>& out) {
   const unsigned off = s.colbyte + (unsigned)r * s.in_row;
@@ -296,8 +368,8 @@ __device__ __forceinline__ void load_row(const Params& p, const Seg<MODE>& s, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) out.v[k] = ld1(s.in[k], off);
   } else {
-    out.v[0] = ld1(s.in[0], off);
-    out.v[1] = ld1(s.in[1], off);
+    out.v[0] = ld_img<T>(s.in[0], off);
+    out.v[1] = ld_img<T>(s.in[1], off);
   }
   out.in = (s.colbyte != kOob) && ((unsigned)r < (unsigned)p.in_h);
 }
@@ -342,7 +414,7 @@ struct Group {
   float xv[4], yv[4];
 };
 
-template <int MODE, bool kVec>
+template <int MODE, bool kVec, int T>
 __device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s, int ri, int lane,
                                             Group<MODE, kVec>& g) {
   g.j = s.j0 + 4 * lane;
@@ -353,21 +425,19 @@ __device__ __forceinline__ void group_begin(const Params& p, const Seg<MODE>& s,
     g.off[t] = (g.ok && (g.j + t) < p.out_w) ? g.base + s.out_elem * t : kOob;
   if constexpr (MODE == kBwd) {
     if constexpr (kVec) {
-      const float4 a = ld4(s.img[0], g.base);
-      const float4 b = ld4(s.img[1], g.base);
-      g.xv[0] = a.x; g.xv[1] = a.y; g.xv[2] = a.z; g.xv[3] = a.w;
-      g.yv[0] = b.x; g.yv[1] = b.y; g.yv[2] = b.z; g.yv[3] = b.w;
+      ld_img4<T>(s.img[0], g.base, g.xv);
+      ld_img4<T>(s.img[1], g.base, g.yv);
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        g.xv[t] = ld1(s.img[0], g.off[t]);
-        g.yv[t] = ld1(s.img[1], g.off[t]);
+        g.xv[t] = ld_img<T>(s.img[0], g.off[t]);
+        g.yv[t] = ld_img<T>(s.img[1], g.off[t]);
       }
     }
   }
 }
 
-template <int MODE, bool kVec, bool kNt>
+template <int MODE, bool kVec, bool kNt, int T>
 __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
                                         const Group<MODE, kVec>& g, const float (&o)[kQ][4],
                                         float dl, double& acc) {
@@ -401,13 +471,13 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
     // a gradient the caller does not want has a zero-size descriptor: its
     // stores are dropped without a branch
     if constexpr (kVec) {
-      st4<kNt>(s.out[0], g.base, make_float4(g1[0], g1[1], g1[2], g1[3]));
-      st4<kNt>(s.out[1], g.base, make_float4(g2[0], g2[1], g2[2], g2[3]));
+      st_img4<T, kNt>(s.out[0], g.base, g1);
+      st_img4<T, kNt>(s.out[1], g.base, g2);
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        st1<kNt>(s.out[0], g.off[t], g1[t]);
-        st1<kNt>(s.out[1], g.off[t], g2[t]);
+        st_img<T, kNt>(s.out[0], g.off[t], g1[t]);
+        st_img<T, kNt>(s.out[1], g.off[t], g2[t]);
       }
     }
   }
@@ -418,7 +488,7 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
 // the row pass and the consumer.  PH = batch index mod 3 fixes the ring slots
 // at compile time.
 
-template <int MODE, bool kVec, bool kNt, int PH>
+template <int MODE, bool kVec, bool kNt, int T, int PH>
 __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
                                       float (&tile)[2][kQ][kRows][kTileW],
                                       float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows], int t,
@@ -428,7 +498,7 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
   const int lane = tid % kWave;
 
   Group<MODE, kVec> g;
-  group_begin<MODE, kVec>(p, s, 4 * t + wave, lane, g);
+  group_begin<MODE, kVec, T>(p, s, 4 * t + wave, lane, g);
 
   Raw<MODE> cur[kRows];
 #pragma unroll
@@ -436,7 +506,7 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
   // prefetch the next batch (rows past the segment are harmless: in range
   // they are real pixels, out of range they read as 0)
 #pragma unroll
-  for (int m = 0; m < kRows; ++m) load_row<MODE>(p, s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
+  for (int m = 0; m < kRows; ++m) load_row<MODE, T>(p, s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
 
   // column pass
 #pragma unroll
@@ -479,10 +549,10 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
       o[q][u] = a;
     }
   }
-  consume<MODE, kVec, kNt>(p, s, g, o, dl, acc);
+  consume<MODE, kVec, kNt, T>(p, s, g, o, dl, acc);
 }
 
-template <int MODE, bool kVec, bool kNt>
+template <int MODE, bool kVec, bool kNt, int T>
 __device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kTileW];
   __shared__ double red[kWaves];
@@ -525,22 +595,26 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     s.nrows = row_end - row_begin;
     s.j0 = strip * kStripOut;
     const int c = s.j0 - p.off + tid;  // this lane's input column
-    s.colbyte = (c >= 0 && c < p.in_w) ? (unsigned)c * 4u : kOob;
-    s.in_row = (unsigned)p.in_pitch * 4u;
+    // the forward reads images of type T; the backward reads fp32 maps
+    constexpr unsigned kInElem = (MODE == kBwd) ? 4u : img_bytes<T>();
+    constexpr unsigned kEb = img_bytes<T>();
+    s.colbyte = (c >= 0 && c < p.in_w) ? (unsigned)c * kInElem : kOob;
+    s.in_row = (unsigned)p.in_pitch * kInElem;
     s.r0 = s.row0 - p.off;
     if constexpr (MODE == kBwd) {
       const float* mp = p.maps + plane * 4 * p.map_plane;
 #pragma unroll
       for (int k = 0; k < 4; ++k) s.in[k] = make_rsrc(mp + k * p.map_plane, p.map_plane * 4);
-      s.img[0] = make_rsrc(p.x + plane * p.img_plane, p.img_plane * 4);
-      s.img[1] = make_rsrc(p.y + plane * p.img_plane, p.img_plane * 4);
-      s.out[0] = make_rsrc(p.gx ? p.gx + plane * p.img_plane : p.x, p.gx ? p.img_plane * 4 : 0);
-      s.out[1] = make_rsrc(p.gy ? p.gy + plane * p.img_plane : p.y, p.gy ? p.img_plane * 4 : 0);
-      s.out_row = (unsigned)p.img_w * 4u;
-      s.out_elem = 4u;
+      const int64_t pb = plane * p.img_plane * kEb;
+      s.img[0] = make_rsrc(byte_ptr(p.x, pb), p.img_plane * kEb);
+      s.img[1] = make_rsrc(byte_ptr(p.y, pb), p.img_plane * kEb);
+      s.out[0] = make_rsrc(p.gx ? byte_ptr(p.gx, pb) : p.x, p.gx ? p.img_plane * kEb : 0);
+      s.out[1] = make_rsrc(p.gy ? byte_ptr(p.gy, pb) : p.y, p.gy ? p.img_plane * kEb : 0);
+      s.out_row = (unsigned)p.img_w * kEb;
+      s.out_elem = kEb;
     } else {
-      s.in[0] = make_rsrc(p.x + plane * p.in_plane, p.in_plane * 4);
-      s.in[1] = make_rsrc(p.y + plane * p.in_plane, p.in_plane * 4);
+      s.in[0] = make_rsrc(byte_ptr(p.x, plane * p.in_plane * kEb), p.in_plane * kEb);
+      s.in[1] = make_rsrc(byte_ptr(p.y, plane * p.in_plane * kEb), p.in_plane * kEb);
       if constexpr (MODE == kFwdTrain) {
         const float* mp = p.maps + plane * 4 * p.map_plane;
 #pragma unroll
@@ -555,21 +629,21 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     Raw<MODE> warm[10];
     Raw<MODE> pre[kRows];
 #pragma unroll
-    for (int k = 0; k < 10; ++k) load_row<MODE>(p, s, s.r0 + k, warm[k]);
+    for (int k = 0; k < 10; ++k) load_row<MODE, T>(p, s, s.r0 + k, warm[k]);
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) load_row<MODE>(p, s, s.r0 + 10 + m, pre[m]);
+    for (int m = 0; m < kRows; ++m) load_row<MODE, T>(p, s, s.r0 + 10 + m, pre[m]);
 #pragma unroll
     for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], p.k_m2, ring[k]);
 
     for (int t = 0;;) {
       if (t >= nb) break;
-      batch<MODE, kVec, kNt, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, kNt, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, kNt, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
       buf ^= 1;
       ++t;
     }
@@ -612,298 +686,56 @@ __device__ __forceinline__ void strip_body(const Params& p) {
   }
 }
 
-// Entry kernels (one per direction, mode and store policy; named for
-// profiles).  "stream" kernels mark their stores non-temporal.
-__global__ __launch_bounds__(kThreads) void ssim_fwd_infer_kernel(const Params p) {
-  strip_body<kFwdInfer, false, false>(p);
-}
-__global__ __launch_bounds__(kThreads) void ssim_fwd_train_kernel(const Params p) {
-  strip_body<kFwdTrain, false, false>(p);
-}
-__global__ __launch_bounds__(kThreads) void ssim_fwd_train_stream_kernel(const Params p) {
-  strip_body<kFwdTrain, false, true>(p);
-}
-__global__ __launch_bounds__(kThreads) void ssim_bwd_kernel(const Params p) {
-  strip_body<kBwd, true, false>(p);
-}
-__global__ __launch_bounds__(kThreads) void ssim_bwd_stream_kernel(const Params p) {
-  strip_body<kBwd, true, true>(p);
-}
-__global__ __launch_bounds__(kThreads) void ssim_bwd_unaligned_kernel(const Params p) {
-  strip_body<kBwd, false, false>(p);
-}
+}  // namespace ssim_dev
 
 // ---------------------------------------------------------------------------
-// Host side
+// Entry kernels: one set per image type (named for profiles; "stream"
+// kernels mark their stores non-temporal), and the table the host launches
+// from, in KernelKind order.
 
-enum KernelId { kKFwdInfer, kKFwdTrain, kKFwdTrainStream, kKBwd, kKBwdStream, kKBwdUnaligned, kKernels };
-const void* const kKernelTable[kKernels] = {
-    (const void*)ssim_fwd_infer_kernel, (const void*)ssim_fwd_train_kernel,
-    (const void*)ssim_fwd_train_stream_kernel, (const void*)ssim_bwd_kernel,
-    (const void*)ssim_bwd_stream_kernel, (const void*)ssim_bwd_unaligned_kernel};
-
-// Bytes a training step touches in HBM (both images, the saved maps, both
-// gradients).  Above this the step cannot stay in the 256 MB last-level
-// cache between the forward and the backward, and the stores stream
-// (non-temporal); below it they stay cacheable so that the backward finds
-// the maps there.
-constexpr size_t kStreamBytes = (size_t)256 << 20;
-
-struct DeviceInfo {
-  bool ready = false;
-  int status = SSIM_OK;
-  int cus = 0;
-  int occ[kKernels] = {};  // resident workgroups per CU, per entry kernel
+namespace ssim_dev {
+enum KernelKind {
+  kKFwdInfer, kKFwdTrain, kKFwdTrainStream, kKBwd, kKBwdStream, kKBwdUnaligned, kKinds
 };
+}  // namespace ssim_dev
 
-constexpr int kMaxDevices = 64;
-std::mutex g_mu;
-DeviceInfo g_dev[kMaxDevices];
-
-int device_info(const DeviceInfo** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SSIM_ERR_HIP;
-  if (dev < 0 || dev >= kMaxDevices) return SSIM_ERR_DEVICE;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceInfo& d = g_dev[dev];
-  if (!d.ready) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SSIM_ERR_HIP;
-    if (prop.warpSize != kWave || strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-      d.status = SSIM_ERR_DEVICE;
-    } else {
-      d.cus = prop.multiProcessorCount;
-      for (int k = 0; k < kKernels; ++k) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kKernelTable[k], kThreads, 0) != hipSuccess)
-          return SSIM_ERR_HIP;
-        d.occ[k] = n > 0 ? n : 1;
-      }
-      d.status = SSIM_OK;
-    }
-    d.ready = true;
-  }
-  *out = &d;
-  return d.status;
-}
-
-int64_t roundup4(int64_t v) { return (v + 3) & ~(int64_t)3; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || na == 0 || nb == 0) return false;
-  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
-  return pa < pb + nb && pb < pa + na;
-}
-
-struct Shape {
-  int64_t N, C, H, W, Ho, Wo, pitch, planes;
-  size_t img_bytes, map_bytes;
-};
-
-int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, Shape* s) {
-  if (padding != SSIM_PAD_VALID && padding != SSIM_PAD_SAME) return SSIM_ERR_PADDING;
-  if (N <= 0 || C <= 0 || H <= 0 || W <= 0) return SSIM_ERR_SHAPE;
-  const int64_t Ho = padding == SSIM_PAD_VALID ? H - 10 : H;
-  const int64_t Wo = padding == SSIM_PAD_VALID ? W - 10 : W;
-  if (Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
-  // Buffer offsets are 32-bit: a plane (image, or map with its row pitch)
-  // holds at most 2^27 elements and a row at most 2^20, so valid offsets
-  // stay below 2^29 and the out-of-range ones (rows above the plane wrap to
-  // just below 2^32; the 2^31 marker plus at most 14 rows of 4 MiB) stay
-  // above 2^30.
-  const int64_t lim = (int64_t)1 << 27;
-  if (W > ((int64_t)1 << 20) || H > lim / W) return SSIM_ERR_OVERFLOW;
-  const int64_t pitch = roundup4(Wo);
-  if (H * W > lim || Ho * pitch > lim) return SSIM_ERR_OVERFLOW;
-  if (N > (int64_t)1 << 40 || C > ((int64_t)1 << 40) / N) return SSIM_ERR_OVERFLOW;
-  const int64_t planes = N * C;
-  // bytes must fit comfortably in 64 bits
-  if (planes > ((int64_t)1 << 58) / (H * W) || planes > ((int64_t)1 << 56) / (Ho * pitch))
-    return SSIM_ERR_OVERFLOW;
-  s->N = N; s->C = C; s->H = H; s->W = W; s->Ho = Ho; s->Wo = Wo; s->pitch = pitch;
-  s->planes = planes;
-  s->img_bytes = (size_t)(planes * H * W) * sizeof(float);
-  s->map_bytes = (size_t)(planes * Ho * pitch) * 4 * sizeof(float);
-  return SSIM_OK;
-}
-
-// Grid: one resident wave of workgroups (CUs x occupancy), or fewer when
-// the work is small.  With fewer strip-columns than resident workgroups,
-// each strip-column is split into `parts` equal row ranges of at least
-// kMinRowsPerBlock rows; otherwise each workgroup takes `per_block` whole
-// strip-columns.
-int plan_grid(const DeviceInfo* d, int which, Params& p) {
-  int64_t resident = (int64_t)d->cus * d->occ[which];
-  if (resident > kMaxBlocks) resident = kMaxBlocks;
-  if (p.cols >= resident) {
-    p.parts = 1;
-    p.per_block = (int)((p.cols + resident - 1) / resident);
-    return (int)((p.cols + p.per_block - 1) / p.per_block);
-  }
-  int64_t parts = resident / p.cols;
-  const int64_t max_parts = (p.out_h + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
-  if (parts > max_parts) parts = max_parts;
-  if (parts < 1) parts = 1;
-  p.parts = (int)parts;
-  p.per_block = 1;
-  return (int)(p.cols * parts);
-}
-
-void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane, int out_h,
-                   int out_w, int off, int64_t planes) {
-  p.in_h = in_h;
-  p.in_w = in_w;
-  p.in_pitch = in_pitch;
-  p.in_plane = in_plane;
-  p.out_h = out_h;
-  p.out_w = out_w;
-  p.off = off;
-  p.strips = (out_w + kStripOut - 1) / kStripOut;
-  p.cols = planes * p.strips;
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// C ABI
-
-extern "C" {
-
-int ssim_abi_version(void) { return SSIM_ABI_VERSION; }
-
-const char* ssim_strerror(int code) {
-  switch (code) {
-    case SSIM_OK: return "success";
-    case SSIM_ERR_NULL: return "a required pointer is NULL";
-    case SSIM_ERR_SHAPE: return "bad shape: N, C, H, W must be positive and valid padding needs H, W >= 11";
-    case SSIM_ERR_PADDING: return "padding must be SSIM_PAD_VALID (0) or SSIM_PAD_SAME (1)";
-    case SSIM_ERR_OVERFLOW: return "a plane holds more than 2^27 elements, a row more than 2^20, or a size overflows";
-    case SSIM_ERR_ALIAS: return "an output buffer overlaps an input or another output";
-    case SSIM_ERR_HIP: return "a HIP runtime call failed";
-    case SSIM_ERR_DEVICE: return "the current device is not a wave64 gfx950 GPU";
-    default: return "unknown error code";
-  }
-}
-
-void ssim_taps(float out[11]) {
-  for (int k = 0; k < 11; ++k) out[k] = tap(k);
-}
-
-int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo) {
-  if (!Ho || !Wo) return SSIM_ERR_NULL;
-  Shape s;
-  const int rc = check_shape(1, 1, H, W, padding, &s);
-  if (rc != SSIM_OK) return rc;
-  *Ho = s.Ho;
-  *Wo = s.Wo;
-  return SSIM_OK;
-}
-
-size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding) {
-  Shape s;
-  if (check_shape(N, C, H, W, padding, &s) != SSIM_OK) return 0;
-  return s.map_bytes;
-}
-
-size_t ssim_workspace_bytes(void) { return sizeof(Workspace); }
-
-int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int64_t H,
-                 int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
-                 void* stream) {
-  if (!img1 || !img2 || !loss || !workspace) return SSIM_ERR_NULL;
-  Shape s;
-  int rc = check_shape(N, C, H, W, padding, &s);
-  if (rc != SSIM_OK) return rc;
-  if (saved_maps && ((uintptr_t)saved_maps & 15u)) return SSIM_ERR_SHAPE;
-  const size_t wsb = sizeof(Workspace);
-  const void* outs[3] = {loss, saved_maps, workspace};
-  const size_t outb[3] = {sizeof(float), saved_maps ? s.map_bytes : 0, wsb};
-  for (int k = 0; k < 3; ++k) {
-    if (overlaps(outs[k], outb[k], img1, s.img_bytes) || overlaps(outs[k], outb[k], img2, s.img_bytes))
-      return SSIM_ERR_ALIAS;
-    for (int l = k + 1; l < 3; ++l)
-      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
+#define SSIM_ENTRY_KERNELS(T, NAME, TABLE)                                                  \
+  namespace {                                                                              \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_infer##NAME##kernel(      \
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kFwdInfer, false, false, T>(p);                          \
+  }                                                                                        \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_train##NAME##kernel(      \
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kFwdTrain, false, false, T>(p);                          \
+  }                                                                                        \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_train_stream##NAME##kernel(\
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kFwdTrain, false, true, T>(p);                           \
+  }                                                                                        \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd##NAME##kernel(            \
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kBwd, true, false, T>(p);                                \
+  }                                                                                        \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd_stream##NAME##kernel(     \
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kBwd, true, true, T>(p);                                 \
+  }                                                                                        \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd_unaligned##NAME##kernel(  \
+      const ssim_dev::Params p) {                                                          \
+    ssim_dev::strip_body<ssim_dev::kBwd, false, false, T>(p);                               \
+  }                                                                                        \
+  }                                                                                        \
+  const void* const* TABLE() {                                                             \
+    static const void* const t[ssim_dev::kKinds] = {                                      \
+        (const void*)ssim_fwd_infer##NAME##kernel, (const void*)ssim_fwd_train##NAME##kernel,\
+        (const void*)ssim_fwd_train_stream##NAME##kernel, (const void*)ssim_bwd##NAME##kernel,\
+        (const void*)ssim_bwd_stream##NAME##kernel,                                        \
+        (const void*)ssim_bwd_unaligned##NAME##kernel};                                    \
+    return t;                                                                              \
   }
 
-  const DeviceInfo* d = nullptr;
-  rc = device_info(&d);
-  if (rc != SSIM_OK) return rc;
-
-  Params p;
-  memset(&p, 0, sizeof(p));
-  const int off = padding == SSIM_PAD_VALID ? 0 : 5;
-  fill_geometry(p, (int)s.H, (int)s.W, (int)s.W, s.H * s.W, (int)s.Ho, (int)s.Wo, off, s.planes);
-  p.x = img1;
-  p.y = img2;
-  p.img_plane = s.H * s.W;
-  p.img_w = (int)s.W;
-  p.maps = saved_maps;
-  p.map_pitch = (int)s.pitch;
-  p.map_plane = s.Ho * s.pitch;
-  const double M = (double)s.planes * (double)s.Ho * (double)s.Wo;
-  p.k_m2 = (float)(-2.0 / M);
-  p.inv_m = 1.0 / M;
-  p.loss = loss;
-  p.ws = static_cast<Workspace*>(workspace);
-
-  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
-  const int which = !saved_maps ? kKFwdInfer : stream_st ? kKFwdTrainStream : kKFwdTrain;
-  const int G = plan_grid(d, which, p);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  void* args[] = {&p};
-  if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
-    return SSIM_ERR_HIP;
-  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
-}
-
-int ssim_backward(const float* dloss, const float* img1, const float* img2, int64_t N,
-                  int64_t C, int64_t H, int64_t W, int padding, const float* saved_maps,
-                  float* grad_img1, float* grad_img2, void* stream) {
-  if (!dloss || !img1 || !img2 || !saved_maps) return SSIM_ERR_NULL;
-  Shape s;
-  int rc = check_shape(N, C, H, W, padding, &s);
-  if (rc != SSIM_OK) return rc;
-  if ((uintptr_t)saved_maps & 15u) return SSIM_ERR_SHAPE;
-  const void* ins[4] = {dloss, img1, img2, saved_maps};
-  const size_t inb[4] = {sizeof(float), s.img_bytes, s.img_bytes, s.map_bytes};
-  float* outs[2] = {grad_img1, grad_img2};
-  for (int k = 0; k < 2; ++k)
-    for (int l = 0; l < 4; ++l)
-      if (overlaps(outs[k], s.img_bytes, ins[l], inb[l])) return SSIM_ERR_ALIAS;
-  if (overlaps(grad_img1, s.img_bytes, grad_img2, s.img_bytes)) return SSIM_ERR_ALIAS;
-  if (!grad_img1 && !grad_img2) return SSIM_OK;
-
-  const DeviceInfo* d = nullptr;
-  rc = device_info(&d);
-  if (rc != SSIM_OK) return rc;
-
-  Params p;
-  memset(&p, 0, sizeof(p));
-  const int off = padding == SSIM_PAD_VALID ? 10 : 5;
-  fill_geometry(p, (int)s.Ho, (int)s.Wo, (int)s.pitch, s.Ho * s.pitch * 4, (int)s.H, (int)s.W,
-                off, s.planes);
-  p.x = img1;
-  p.y = img2;
-  p.img_plane = s.H * s.W;
-  p.img_w = (int)s.W;
-  p.maps = const_cast<float*>(saved_maps);
-  p.map_pitch = (int)s.pitch;
-  p.map_plane = s.Ho * s.pitch;
-  p.dloss = dloss;
-  p.gx = grad_img1;
-  p.gy = grad_img2;
-  p.k_m2 = (float)(-2.0 / ((double)s.planes * (double)s.Ho * (double)s.Wo));
-
-  const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % 16 == 0) && ((uintptr_t)img2 % 16 == 0) &&
-                   ((uintptr_t)grad_img1 % 16 == 0) && ((uintptr_t)grad_img2 % 16 == 0);
-  const bool stream_st = 4 * s.img_bytes + s.map_bytes > kStreamBytes;
-  const int which = !vec ? kKBwdUnaligned : stream_st ? kKBwdStream : kKBwd;
-  const int G = plan_grid(d, which, p);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  void* args[] = {&p};
-  if (hipLaunchKernel(kKernelTable[which], dim3(G), dim3(kThreads), args, 0, st) != hipSuccess)
-    return SSIM_ERR_HIP;
-  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
-}
-
-}  // extern "C"
+// Kernel tables exported by the per-type translation units.
+const void* const* ssim_kernel_table_f32();
+const void* const* ssim_kernel_table_f16();
+const void* const* ssim_kernel_table_bf16();

@@ -23,8 +23,9 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ["ssim_forward", "ssim_backward", "ssim_saved_maps_bytes", "ssim_workspace_bytes",
-              "ssim_strerror", "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
+    for n in ["ssim_forward", "ssim_backward", "ssim_forward_typed", "ssim_backward_typed",
+              "ssim_saved_maps_bytes", "ssim_workspace_bytes", "ssim_strerror",
+              "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
         assert n in names
 
 
@@ -35,8 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert S.ssim_abi_version() == 1
-    for code in range(0, -8, -1):
+    assert S.ssim_abi_version() == 2
+    for code in range(0, -9, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
 
@@ -104,6 +105,35 @@ def test_backward_argument_errors_return_before_any_hip_call():
     assert _bwd(lib, g1=None, g2=None) == 0           # nothing to do: no launch
 
 
+def test_typed_entry_points_validate_dtype_and_alignment():
+    lib = S.lib()
+    fwd = lambda dt, **kw: lib.ssim_forward_typed(
+        kw.get("img1", 0x1000), 0x100000, dt, 1, 1, 64, kw.get("W", 64), 0, 0x200000,
+        kw.get("maps", 0x300000), 0x900000, None)
+    bwd = lambda dt: lib.ssim_backward_typed(0x1000, 0x10000, 0x100000, dt, 1, 1, 64, 64, 0,
+                                             0x300000, 0x900000, 0xA00000, None)
+    for dt in (3, -1, 99):
+        assert fwd(dt) == -8
+        assert bwd(dt) == -8
+    assert fwd(1, img1=None) == -1
+    assert fwd(2, W=10) == -2
+    assert fwd(1, maps=0x300008) == -2
+    assert fwd(1, img1=0x1001) == -2          # a half image must be 2-byte aligned
+    assert _fwd(lib, img1=0x1002) == -2       # an fp32 image 4-byte aligned
+    assert _bwd(lib, g1=0x900002) == -2
+    # a half-precision plane of 2^27 elements is still the limit
+    assert lib.ssim_forward_typed(0x1000, 0x100000, 1, 1, 1, (1 << 14) + 1, 1 << 13, 0,
+                                  0x200000, None, 0x900000, None) == -4
+
+
+def test_typed_overlap_uses_element_size():
+    lib = S.lib()
+    # a 64x64 fp16 image at 0x10000 spans 8 KiB; a loss 4 KiB in overlaps it
+    assert lib.ssim_forward_typed(0x10000, 0x100000, 1, 1, 1, 64, 64, 0, 0x10000 + 4096,
+                                  None, 0x900000, None) == -5
+    assert S.ssim_strerror(-8)
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
 
@@ -112,3 +142,5 @@ def test_python_binding_rejects_cpu_tensors():
         S.ssim_loss(x, x)
     with pytest.raises(TypeError):
         S.ssim_loss(x.double(), x.double())
+    with pytest.raises(TypeError):
+        S.ssim_loss(x.half(), x.half())
