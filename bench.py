@@ -1,17 +1,23 @@
-"""Throughput of the fused SSIM loss, forward + backward, fp32, on one MI355X.
+"""Throughput of the fused SSIM loss, forward + backward, on one MI355X.
 
-One step = ssim_forward (training mode: loss + saved maps) followed by
-ssim_backward (both image gradients) on one batch of synthetic images already
-resident in HBM, through the C ABI on torch's current stream.
+One step = one forward + backward of the chosen design (--design) on one batch
+of synthetic images already resident in HBM, through the C ABI on torch's
+current stream:
+  saved     : ssim_forward (training mode: loss + saved maps), then
+              ssim_backward (both image gradients)
+  recompute : ssim_forward (inference: loss only), then
+              ssim_backward_recompute (both gradients, no maps)
+  one-pass  : ssim_loss_and_grad (loss and both gradients in one launch)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--dtype float32|float16|bfloat16]
+                    [--dtype float32|float16|bfloat16] [--design NAME] [--all-kernels]
 
 Prints one JSON line: metric Mpix/s (pixels = N*H*W per step, wall clock over
 K steps), the roofline of the dominant kernel (algorithmic bytes per launch /
 average launch time from HIP events around K back-to-back launches of that
-kernel on the stream it runs on), and the fp64 CPU oracle's throughput on a
-bounded sample of the same workload.
+kernel on the stream it runs on), per-design step times when their kernels
+were timed, and the fp64 CPU oracle's throughput on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -39,6 +45,12 @@ def parse():
     ap.add_argument("--workload", default="1080p-valid")
     ap.add_argument("--dtype", default="float32", choices=["float32", "float16", "bfloat16"],
                     help="storage type of images and gradients (arithmetic is fp32)")
+    ap.add_argument("--design", default="saved", choices=["saved", "recompute", "one-pass"],
+                    help="saved: forward saves the statistics, backward reads them; "
+                         "recompute: loss-only forward, backward recomputes the statistics; "
+                         "one-pass: loss and gradients in one launch")
+    ap.add_argument("--all-kernels", action="store_true",
+                    help="also time the kernels of the other designs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with a cache flush before each (0 = skip)")
@@ -61,20 +73,23 @@ def algorithmic_bytes(shape, padding, eb=4):
     images and gradients of eb bytes per element: forward reads x, y (2 eb per
     input element) and writes four fp32 maps (16 B per map entry); backward
     reads the maps (16 B per entry), x and y (2 eb per element) and writes
-    both gradients (2 eb per element)."""
+    both gradients (2 eb per element).  The recomputing kernels read x, y and
+    write both gradients (4 eb per element); the inference forward reads x, y."""
     N, C, H, W = shape
     Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
     e_in = N * C * H * W
     e_out = N * C * Ho * Wo
     return {"ssim_forward": 2 * eb * e_in + 16 * e_out,
             "ssim_backward": 16 * e_out + 4 * eb * e_in,
-            "ssim_forward(inference)": 2 * eb * e_in}
+            "ssim_forward(inference)": 2 * eb * e_in,
+            "ssim_backward_recompute": 4 * eb * e_in,
+            "ssim_loss_and_grad": 4 * eb * e_in}
 
 
 def cpu_baseline(x, y, padding, pixels_per_image_batch):
     """The fp64 oracle, as it stands, on the host cores: whole forward +
     gradient of the same workload, repeated until about 10 s have passed
-    (at most 4 times)."""
+    (at most 200 times)."""
     import oracle
 
     try:
@@ -88,7 +103,7 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch):
         oracle.ssim_loss(x, y, padding)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or reps >= 4:
+        if el >= 10.0 or reps >= 200:
             break
     return {
         "value": round(reps * pixels_per_image_batch / el / 1e6, 3),
@@ -98,6 +113,14 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch):
         "sample": f"{reps} x whole forward+gradient of the benchmark batch "
                   f"({x.shape}, {padding}) in {el:.1f} s",
     }
+
+
+DESIGNS = {
+    # design: the launches of one step
+    "saved": ("ssim_forward", "ssim_backward"),
+    "recompute": ("ssim_forward(inference)", "ssim_backward_recompute"),
+    "one-pass": ("ssim_loss_and_grad",),
+}
 
 
 def main():
@@ -123,22 +146,34 @@ def main():
     t1 = torch.from_numpy(x).to(dev).to(tdtype).contiguous()
     t2 = torch.from_numpy(y).to(dev).to(tdtype).contiguous()
     loss = torch.empty((), dtype=torch.float32, device=dev)
-    maps = S.alloc_saved_maps(t1, w.padding)
+    maps = S.alloc_saved_maps(t1, w.padding) if args.design == "saved" or args.all_kernels else None
     ws = S.workspace_for(dev)
     dloss = torch.tensor(0.8, dtype=torch.float32, device=dev)  # as under a weighted loss
     g1 = torch.empty_like(t1)
     g2 = torch.empty_like(t2)
     torch.cuda.synchronize()
 
+    launches = {
+        "ssim_forward": lambda: S.ssim_forward(t1, t2, w.padding, loss, maps, ws),
+        "ssim_backward": lambda: S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2),
+        "ssim_forward(inference)": lambda: S.ssim_forward(t1, t2, w.padding, loss, None, ws),
+        "ssim_backward_recompute":
+            lambda: S.ssim_backward_recompute(dloss, t1, t2, w.padding, g1, g2),
+        "ssim_loss_and_grad":
+            lambda: S.ssim_loss_and_grad(t1, t2, w.padding, dloss, loss, ws, g1, g2),
+    }
+    step_launches = [launches[k] for k in DESIGNS[args.design]]
+
     def step():
-        S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
-        S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+        for f in step_launches:
+            f()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # the step: K forward+backward pairs, wall clock between two synchronisations
+    # the step: K passes of the design's launches, wall clock between two
+    # synchronisations
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -153,6 +188,8 @@ def main():
     # per-kernel launch time: K launches of one kernel back to back between two
     # HIP events on the stream the kernels run on (torch's current stream)
     def per_launch_ms(fn):
+        for _ in range(3):
+            fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(K):
@@ -161,30 +198,26 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    fwd_ms = per_launch_ms(lambda: S.ssim_forward(t1, t2, w.padding, loss, maps, ws))
-    bwd_ms = per_launch_ms(lambda: S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2))
-    # inference forward: the loss only, nothing saved for a backward
-    inf_ms = per_launch_ms(lambda: S.ssim_forward(t1, t2, w.padding, loss, None, ws))
+    timed = [k for k in launches if (maps is not None or k not in ("ssim_forward", "ssim_backward"))
+             and (args.all_kernels or k in DESIGNS[args.design])]
+    kern = {k: per_launch_ms(launches[k]) for k in timed}
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
     if args.cold_steps > 0:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        cf, cb = [], []
+        times = []
         for _ in range(args.cold_steps):
             flush.fill_(1.0)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record()
-            S.ssim_forward(t1, t2, w.padding, loss, maps, ws)
-            e[1].record()
-            S.ssim_backward(dloss, t1, t2, w.padding, maps, g1, g2)
-            e[2].record()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
             torch.cuda.synchronize()
-            cf.append(e[0].elapsed_time(e[1]))
-            cb.append(e[1].elapsed_time(e[2]))
+            times.append(e0.elapsed_time(e1))
         del flush
-        cold = {"fwd_ms": round(sum(cf) / len(cf), 5), "bwd_ms": round(sum(cb) / len(cb), 5),
-                "mpix_per_s": round(mpix / ((sum(cf) + sum(cb)) / len(cf) / 1e3), 1)}
+        cms = sum(times) / len(times)
+        cold = {"ms_per_step": round(cms, 5), "mpix_per_s": round(mpix / (cms * 1e-3), 1)}
 
     if args.copy_calib > 0:
         n = args.copy_calib * (1 << 20) // 4
@@ -195,8 +228,7 @@ def main():
         torch.cuda.synchronize()
 
     alg = algorithmic_bytes((N, C, H, W), w.padding, eb)
-    kern = {"ssim_forward": fwd_ms, "ssim_backward": bwd_ms}
-    dom = max(kern, key=kern.get)
+    dom = max(DESIGNS[args.design], key=lambda k: kern[k])
     achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
 
     # HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
@@ -213,6 +245,17 @@ def main():
                 and dom in tr.get("bytes_per_launch", {})):
             traffic = tr["bytes_per_launch"][dom]
 
+    # every design whose launches were all timed: its step from the per-kernel
+    # times, and its algorithmic HBM rate
+    designs = {}
+    for d, ks in DESIGNS.items():
+        if all(k in kern for k in ks):
+            ms = sum(kern[k] for k in ks)
+            by = sum(alg[k] for k in ks)
+            designs[d] = {"ms_per_step": round(ms, 5), "mpix_per_s": round(mpix / (ms * 1e-3), 1),
+                          "hbm_bytes_per_elem": round(by / (N * C * H * W), 2),
+                          "algorithmic_gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+
     out = {
         "metric": "Mpix/s fused SSIM fwd+bwd fp32 at 1080p; achieved HBM GB/s as % of peak",
         "value": round(value, 1),
@@ -228,7 +271,8 @@ def main():
         "dtype": {"float32": "f32", "float16": "f16 I/O, f32 math",
                   "bfloat16": "bf16 I/O, f32 math"}[args.dtype],
         "data": "synthetic",
-        "config": {"workload": args.workload, "shape": [N, C, H, W], "padding": w.padding},
+        "config": {"workload": args.workload, "shape": [N, C, H, W], "padding": w.padding,
+                   "design": args.design},
         "roofline": {
             "bound": "hbm",
             "kernel": dom,
@@ -239,12 +283,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": alg[dom],
         },
-        "kernels_ms": {"ssim_forward": round(fwd_ms, 5), "ssim_backward": round(bwd_ms, 5),
-                       "ssim_forward(inference)": round(inf_ms, 5)},
-        "inference": {"mpix_per_s": round(mpix / (inf_ms * 1e-3), 1),
-                      "hbm_gbs": round(alg["ssim_forward(inference)"] / (inf_ms * 1e-3) / 1e9, 1)},
-        "step_hbm_gbs": round((alg["ssim_forward"] + alg["ssim_backward"]) /
-                              ((fwd_ms + bwd_ms) * 1e-3) / 1e9, 1),
+        "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+        "designs": designs,
         "cold": cold,
         "loss": float(loss.item()),
     }

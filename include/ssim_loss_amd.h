@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 2
+#define SSIM_ABI_VERSION 3
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -156,6 +156,43 @@ int ssim_forward_typed(const void* img1, const void* img2, int dtype, int64_t N,
 int ssim_backward_typed(const float* dloss, const void* img1, const void* img2, int dtype,
                         int64_t N, int64_t C, int64_t H, int64_t W, int padding,
                         const float* saved_maps, void* grad_img1, void* grad_img2, void* stream);
+
+/* Backward without saved maps.  Same result as ssim_backward (the adjoint of
+ * the blur and the chain rule of "TriSSIM", How it works), but the blurred
+ * statistics are formed again from the images instead of being read from a
+ * forward's saved maps: pair it with an inference-mode ssim_forward
+ * (saved_maps = NULL).  It moves only the images and the gradients through
+ * HBM and needs no map buffer, at about twice the arithmetic.
+ *
+ *   dloss        : device fp32 scalar, the upstream gradient of the loss
+ *   img1, img2   : device images of `dtype` (inputs)
+ *   dtype, N..padding : as for ssim_forward_typed
+ *   grad_img1/2  : device outputs of `dtype`, or NULL to skip (both NULL: no-op)
+ *   stream       : hipStream_t (NULL = default stream) */
+int ssim_backward_recompute(const float* dloss, const void* img1, const void* img2, int dtype,
+                            int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                            void* grad_img1, void* grad_img2, void* stream);
+
+/* Loss and gradients in one pass: the forward (loss = 1 - mean SSIM, as
+ * ssim_forward) and the backward (as ssim_backward, scaled by *dloss) of one
+ * training step in a single launch, for callers that know the upstream
+ * gradient before the forward -- the weight of the SSIM term in a training
+ * loss, or 1.  Reads the images once and writes the gradients; no map
+ * buffer.
+ *
+ *   img1, img2   : device images of `dtype` (inputs)
+ *   dtype, N..padding : as for ssim_forward_typed
+ *   dloss        : device fp32 scalar, read before any gradient is formed
+ *   loss         : device fp32 scalar (output; required)
+ *   workspace    : as for ssim_forward (the same rules: zeroed once, not
+ *                  shared by calls that may overlap)
+ *   grad_img1/2  : device outputs of `dtype`, or NULL to skip
+ *   stream       : hipStream_t (NULL = default stream)
+ * Deterministic, like ssim_forward; the loss equals ssim_forward's up to the
+ * order of the fp64 summation. */
+int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
+                       int64_t H, int64_t W, int padding, const float* dloss, float* loss,
+                       void* workspace, void* grad_img1, void* grad_img2, void* stream);
 
 #ifdef __cplusplus
 }

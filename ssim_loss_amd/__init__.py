@@ -11,11 +11,18 @@ bfloat16 tensors; the C functions ssim_forward_typed / ssim_backward_typed
 are called for the half types):
   ssim_forward(img1, img2, padding, loss, saved_maps, workspace)
   ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2)
+  ssim_backward_recompute(dloss, img1, img2, padding, grad_img1, grad_img2)
+  ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, grad_img2)
   ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
   ssim_strerror, ssim_abi_version
 Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
-  ssim_loss(img1, img2, padding="valid", train=True) -> 1 - mean SSIM
+  ssim_loss(img1, img2, padding="valid", train=True, recompute=False)
+      -> 1 - mean SSIM; recompute=True keeps no maps between forward and
+         backward (the backward forms the statistics again from the images)
   fused_ssim(img1, img2, padding="same", train=True)  -> mean SSIM
+One-pass step, for an upstream gradient known in advance:
+  loss_and_grad(img1, img2, padding="valid", weight=1.0)
+      -> (weight-free loss, weight * dloss/dimg1, weight * dloss/dimg2)
 """
 from __future__ import annotations
 
@@ -74,6 +81,12 @@ def lib() -> ctypes.CDLL:
         L.ssim_backward_typed.restype = i32
         L.ssim_backward_typed.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp,
                                           vp]
+        L.ssim_backward_recompute.restype = i32
+        L.ssim_backward_recompute.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp,
+                                              vp]
+        L.ssim_loss_and_grad.restype = i32
+        L.ssim_loss_and_grad.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
+                                         vp]
         _lib = L
     return _lib
 
@@ -192,6 +205,42 @@ def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) 
         raise SsimError(rc, "ssim_backward")
 
 
+def _check_pair_and_grads(img1, img2, grads):
+    _check_image(img1, "img1")
+    _check_image(img2, "img2")
+    if img1.shape != img2.shape:
+        raise ValueError("img1 and img2 must have the same shape")
+    if img1.dtype != img2.dtype:
+        raise TypeError("img1 and img2 must have the same dtype")
+    for g in grads:
+        if g is not None and (g.dtype != img1.dtype or g.shape != img1.shape):
+            raise TypeError("gradients must have the images' dtype and shape")
+
+
+def ssim_backward_recompute(dloss, img1, img2, padding, grad_img1, grad_img2) -> None:
+    """Calls the C ``ssim_backward_recompute`` (no saved maps) on torch's
+    current stream."""
+    _check_pair_and_grads(img1, img2, (grad_img1, grad_img2))
+    N, C, H, W = img1.shape
+    rc = lib().ssim_backward_recompute(_dptr(dloss), _dptr(img1), _dptr(img2), _dtype_code(img1),
+                                       N, C, H, W, _pad(padding), _dptr(grad_img1),
+                                       _dptr(grad_img2), _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_backward_recompute")
+
+
+def ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, grad_img2) -> None:
+    """Calls the C ``ssim_loss_and_grad`` (loss and gradients in one launch)
+    on torch's current stream."""
+    _check_pair_and_grads(img1, img2, (grad_img1, grad_img2))
+    N, C, H, W = img1.shape
+    rc = lib().ssim_loss_and_grad(_dptr(img1), _dptr(img2), _dtype_code(img1), N, C, H, W,
+                                  _pad(padding), _dptr(dloss), _dptr(loss), _dptr(workspace),
+                                  _dptr(grad_img1), _dptr(grad_img2), _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_loss_and_grad")
+
+
 # --------------------------------------------------------------------------- buffers
 _workspaces: dict = {}
 
@@ -225,29 +274,39 @@ def _make_function():
 
     class _SsimLoss(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, img1, img2, padding, train):
+        def forward(ctx, img1, img2, padding, train, recompute):
             img1 = img1.detach()
             img2 = img2.detach()
             loss = torch.empty((), dtype=torch.float32, device=img1.device)
-            maps = alloc_saved_maps(img1, padding) if train else None
+            maps = alloc_saved_maps(img1, padding) if train and not recompute else None
             ssim_forward(img1, img2, padding, loss, maps, workspace_for(img1.device))
             ctx.padding = padding
             ctx.train = train
+            ctx.recompute = recompute
             if train:
-                ctx.save_for_backward(img1, img2, maps)
+                if recompute:
+                    ctx.save_for_backward(img1, img2)
+                else:
+                    ctx.save_for_backward(img1, img2, maps)
             return loss
 
         @staticmethod
         def backward(ctx, dloss):
             if not ctx.train:
                 raise RuntimeError("ssim_loss was called with train=False; no gradient saved")
-            img1, img2, maps = ctx.saved_tensors
             want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
-            g1 = torch.empty_like(img1) if want1 else None
-            g2 = torch.empty_like(img2) if want2 else None
             dl = dloss.detach().to(dtype=torch.float32).contiguous()
-            ssim_backward(dl, img1, img2, ctx.padding, maps, g1, g2)
-            return g1, g2, None, None
+            if ctx.recompute:
+                img1, img2 = ctx.saved_tensors
+                g1 = torch.empty_like(img1) if want1 else None
+                g2 = torch.empty_like(img2) if want2 else None
+                ssim_backward_recompute(dl, img1, img2, ctx.padding, g1, g2)
+            else:
+                img1, img2, maps = ctx.saved_tensors
+                g1 = torch.empty_like(img1) if want1 else None
+                g2 = torch.empty_like(img2) if want2 else None
+                ssim_backward(dl, img1, img2, ctx.padding, maps, g1, g2)
+            return g1, g2, None, None, None
 
     return _SsimLoss
 
@@ -255,9 +314,11 @@ def _make_function():
 _fn = None
 
 
-def ssim_loss(img1, img2, padding: str = "valid", train: bool = True):
+def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute: bool = False):
     """loss = 1 - mean SSIM (a 0-d fp32 tensor on the images' device), with
-    gradients for whichever of img1 / img2 requires them."""
+    gradients for whichever of img1 / img2 requires them.  recompute=True
+    saves no maps for the backward (16 bytes per map entry less memory) and
+    forms the statistics again from the images when the gradient is taken."""
     global _fn
     if _fn is None:
         _fn = _make_function()
@@ -268,10 +329,32 @@ def ssim_loss(img1, img2, padding: str = "valid", train: bool = True):
     if img1.dtype != img2.dtype:
         raise TypeError("img1 and img2 must have the same dtype")
     _pad(padding)
-    return _fn.apply(img1, img2, padding, bool(train))
+    return _fn.apply(img1, img2, padding, bool(train), bool(recompute))
 
 
 def fused_ssim(img1, img2, padding: str = "same", train: bool = True):
     """Mean SSIM ("Fully Fused Differentiable SSIM", Usage: default padding
     "same")."""
     return 1.0 - ssim_loss(img1, img2, padding, train)
+
+
+def loss_and_grad(img1, img2, padding: str = "valid", weight=1.0, grad1: bool = True,
+                  grad2: bool = True):
+    """One launch for a training step whose upstream gradient is known before
+    the forward: returns (loss, grad_img1, grad_img2) with loss = 1 - mean
+    SSIM and grad = weight * d loss / d img (None where not asked for).
+    `weight` is a number or a 0-d device tensor (e.g. the SSIM term's weight
+    in a training loss)."""
+    import torch
+
+    _check_pair_and_grads(img1, img2, ())
+    dev = img1.device
+    if isinstance(weight, torch.Tensor):
+        dl = weight.detach().to(device=dev, dtype=torch.float32).reshape(()).contiguous()
+    else:
+        dl = torch.tensor(float(weight), dtype=torch.float32, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    g1 = torch.empty_like(img1) if grad1 else None
+    g2 = torch.empty_like(img2) if grad2 else None
+    ssim_loss_and_grad(img1.detach(), img2.detach(), padding, dl, loss, workspace_for(dev), g1, g2)
+    return loss, g1, g2

@@ -9,7 +9,7 @@
 
 #include <mutex>
 
-#include "ssim_device.hpp"
+#include "ssim_entry.hpp"
 #include "ssim_loss_amd.h"
 
 namespace {
@@ -126,7 +126,7 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int padding, int dty
 // each strip-column is split into `parts` equal row ranges of at least
 // kMinRowsPerBlock rows; otherwise each workgroup takes `per_block` whole
 // strip-columns.
-int plan_grid(const DeviceInfo* d, int dtype, int which, Params& p) {
+int plan_grid(const DeviceInfo* d, int dtype, int which, Params& p, int min_rows) {
   int64_t resident = (int64_t)d->cus * d->occ[dtype][which];
   if (resident > kMaxBlocks) resident = kMaxBlocks;
   if (p.cols >= resident) {
@@ -135,7 +135,7 @@ int plan_grid(const DeviceInfo* d, int dtype, int which, Params& p) {
     return (int)((p.cols + p.per_block - 1) / p.per_block);
   }
   int64_t parts = resident / p.cols;
-  const int64_t max_parts = (p.out_h + kMinRowsPerBlock - 1) / kMinRowsPerBlock;
+  const int64_t max_parts = (p.out_h + min_rows - 1) / min_rows;
   if (parts > max_parts) parts = max_parts;
   if (parts < 1) parts = 1;
   p.parts = (int)parts;
@@ -156,8 +156,9 @@ void fill_geometry(Params& p, int in_h, int in_w, int in_pitch, int64_t in_plane
   p.cols = planes * p.strips;
 }
 
-int launch(const DeviceInfo* d, int dtype, int which, Params& p, void* stream) {
-  const int G = plan_grid(d, dtype, which, p);
+int launch(const DeviceInfo* d, int dtype, int which, Params& p, void* stream,
+           int min_rows = kMinRowsPerBlock) {
+  const int G = plan_grid(d, dtype, which, p, min_rows);
   void* args[] = {&p};
   if (hipLaunchKernel(kernel_table(dtype)[which], dim3(G), dim3(kThreads), args, 0,
                       static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -260,6 +261,76 @@ int backward_impl(const float* dloss, const void* img1, const void* img2, int dt
   return launch(d, dtype, which, p, stream);
 }
 
+// The recomputing kernels read only the images: the backward without saved
+// maps (loss == NULL) and the one-pass loss and gradients (loss != NULL).
+// A row range of n gradient rows reads n + 20 image rows, so ranges are kept
+// at least kRecompMinRows long.
+constexpr int kRecompMinRows = 40;
+
+int recompute_impl(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
+                   int64_t C, int64_t H, int64_t W, int padding, float* loss, void* workspace,
+                   void* grad_img1, void* grad_img2, void* stream) {
+  if (!dloss || !img1 || !img2) return SSIM_ERR_NULL;
+  if (loss && !workspace) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if (misaligned(img1, dtype) || misaligned(img2, dtype) || misaligned(grad_img1, dtype) ||
+      misaligned(grad_img2, dtype))
+    return SSIM_ERR_SHAPE;
+  const void* ins[3] = {dloss, img1, img2};
+  const size_t inb[3] = {sizeof(float), s.img_bytes, s.img_bytes};
+  const void* outs[4] = {grad_img1, grad_img2, loss, workspace};
+  const size_t outb[4] = {s.img_bytes, s.img_bytes, sizeof(float),
+                          loss ? sizeof(Workspace) : 0};
+  for (int k = 0; k < 4; ++k) {
+    for (int l = 0; l < 3; ++l)
+      if (overlaps(outs[k], outb[k], ins[l], inb[l])) return SSIM_ERR_ALIAS;
+    for (int l = k + 1; l < 4; ++l)
+      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
+  }
+  if (!loss && !grad_img1 && !grad_img2) return SSIM_OK;
+
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.in_h = (int)s.H;
+  p.in_w = (int)s.W;
+  p.in_pitch = (int)s.W;
+  p.in_plane = s.H * s.W;
+  p.out_h = (int)s.H;  // gradient extent
+  p.out_w = (int)s.W;
+  p.off = padding == SSIM_PAD_VALID ? 0 : 5;    // image -> map
+  p.off2 = padding == SSIM_PAD_VALID ? 10 : 5;  // map -> gradient (the adjoint)
+  p.map_h = (int)s.Ho;
+  p.map_w = (int)s.Wo;
+  p.strips = (int)((s.W + kFOut - 1) / kFOut);
+  p.cols = s.planes * p.strips;
+  p.x = img1;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.dloss = dloss;
+  p.gx = grad_img1;
+  p.gy = grad_img2;
+  const double M = (double)s.planes * (double)s.Ho * (double)s.Wo;
+  p.k_m2 = (float)(-2.0 / M);
+  p.inv_m = 1.0 / M;
+  p.loss = loss;
+  p.ws = static_cast<Workspace*>(workspace);
+
+  const uintptr_t al = (uintptr_t)(4 * elem_bytes(dtype));
+  const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % al == 0) && ((uintptr_t)img2 % al == 0) &&
+                   ((uintptr_t)grad_img1 % al == 0) && ((uintptr_t)grad_img2 % al == 0);
+  const bool stream_st = 4 * s.img_bytes > kStreamBytes;
+  const int which = loss ? (!vec ? kKLossGradUnaligned : stream_st ? kKLossGradStream : kKLossGrad)
+                         : (!vec ? kKRecompUnaligned : stream_st ? kKRecompStream : kKRecomp);
+  return launch(d, dtype, which, p, stream, kRecompMinRows);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -331,6 +402,21 @@ int ssim_backward_typed(const float* dloss, const void* img1, const void* img2, 
                         const float* saved_maps, void* grad_img1, void* grad_img2, void* stream) {
   return backward_impl(dloss, img1, img2, dtype, N, C, H, W, padding, saved_maps, grad_img1,
                        grad_img2, stream);
+}
+
+int ssim_backward_recompute(const float* dloss, const void* img1, const void* img2, int dtype,
+                            int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                            void* grad_img1, void* grad_img2, void* stream) {
+  return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, nullptr, nullptr, grad_img1,
+                        grad_img2, stream);
+}
+
+int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
+                       int64_t H, int64_t W, int padding, const float* dloss, float* loss,
+                       void* workspace, void* grad_img1, void* grad_img2, void* stream) {
+  if (!loss) return SSIM_ERR_NULL;
+  return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
+                        grad_img2, stream);
 }
 
 }  // extern "C"

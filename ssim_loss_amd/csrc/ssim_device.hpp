@@ -174,6 +174,10 @@ struct Params {
   const float* dloss;
   void* gx;             // of the kernel's image type
   void* gy;
+  // recomputing kernels (image -> map -> gradient in one pass): off is the
+  // forward's offset, off2 the adjoint's; the map extent
+  int off2;
+  int map_h, map_w;
 };
 
 // ---------------------------------------------------------------------------
@@ -552,6 +556,75 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
   consume<MODE, kVec, kNt, T>(p, s, g, o, dl, acc);
 }
 
+// Workgroup sum of the map of 1 - S, then the last workgroup to finish
+// forms the mean: loss = sum / M.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kWaves],
+                                            int& is_last) {
+  const int tid = threadIdx.x;
+  const int G = gridDim.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double bs = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) bs += red[w];
+    // Publish the partial with a device-coherent atomic store and wait for
+    // its acknowledgement before taking the ticket: a release of exactly
+    // this one value.  (A release fence would also write back every dirty
+    // line of this XCD's L2 -- megabytes of map stores -- in every
+    // workgroup.)
+    __hip_atomic_store(&p.ws->partial[blockIdx.x], bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned prev =
+        __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == (unsigned)(G - 1));
+  }
+  __syncthreads();
+  if (is_last && wave == 0) {
+    double sum = 0.0;
+    for (int k = lane; k < G; k += kWave)
+      sum += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (lane == 0) {
+      *p.loss = (float)(sum * p.inv_m);
+      __hip_atomic_store(&p.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// This workgroup's share of the grid: one row range of one strip-column, or
+// a run of whole strip-columns.  Workgroup ids are first remapped so that
+// each XCD (hardware hands consecutive ids to the 8 XCDs in turn) owns one
+// contiguous eighth of the work.
+struct Share {
+  int64_t sc_begin, sc_end;
+  int row_begin, row_end;
+};
+
+__device__ __forceinline__ Share work_share(const Params& p, int rows) {
+  const int G = gridDim.x;
+  int lb = blockIdx.x;
+  if ((G & 7) == 0) lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  Share w;
+  if (p.parts > 1) {
+    w.sc_begin = lb / p.parts;
+    w.sc_end = w.sc_begin + 1;
+    const int part = lb - (int)w.sc_begin * p.parts;
+    w.row_begin = (int)((int64_t)part * rows / p.parts);
+    w.row_end = (int)((int64_t)(part + 1) * rows / p.parts);
+  } else {
+    w.sc_begin = (int64_t)lb * p.per_block;
+    w.sc_end = w.sc_begin + p.per_block < p.cols ? w.sc_begin + p.per_block : p.cols;
+    w.row_begin = 0;
+    w.row_end = rows;
+  }
+  return w;
+}
+
 template <int MODE, bool kVec, bool kNt, int T>
 __device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kTileW];
@@ -559,28 +632,11 @@ __device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ int is_last;
 
   const int tid = threadIdx.x;
-  const int G = gridDim.x;
-  // XCD-aware order: hardware hands consecutive workgroup ids to the 8 XCDs
-  // in turn; give each XCD one contiguous eighth of the work.
-  int lb = blockIdx.x;
-  if ((G & 7) == 0) lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  // This workgroup's share: one row range of one strip-column, or a run of
-  // whole strip-columns.  Every workgroup gets the same amount of work, so
-  // the grid (one resident wave of workgroups) finishes together.
-  int64_t sc_begin, sc_end;
-  int row_begin, row_end;
-  if (p.parts > 1) {
-    sc_begin = lb / p.parts;
-    sc_end = sc_begin + 1;
-    const int part = lb - (int)sc_begin * p.parts;
-    row_begin = (int)((int64_t)part * p.out_h / p.parts);
-    row_end = (int)((int64_t)(part + 1) * p.out_h / p.parts);
-  } else {
-    sc_begin = (int64_t)lb * p.per_block;
-    sc_end = sc_begin + p.per_block < p.cols ? sc_begin + p.per_block : p.cols;
-    row_begin = 0;
-    row_end = p.out_h;
-  }
+  // Every workgroup gets the same amount of work, so the grid (one resident
+  // wave of workgroups) finishes together.
+  const Share w = work_share(p, p.out_h);
+  const int64_t sc_begin = w.sc_begin, sc_end = w.sc_end;
+  const int row_begin = w.row_begin, row_end = w.row_end;
 
   float dl = 0.0f;
   if constexpr (MODE == kBwd) dl = *p.dloss;
@@ -649,93 +705,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     }
   }
 
-  if constexpr (MODE != kBwd) {
-    // workgroup sum of the map of 1 - S, then the last workgroup finishes the mean
-    const int wave = tid / kWave, lane = tid % kWave;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    if (lane == 0) red[wave] = acc;
-    __syncthreads();
-    if (tid == 0) {
-      double bs = 0.0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) bs += red[w];
-      // Publish the partial with a device-coherent atomic store and wait for
-      // its acknowledgement before taking the ticket: a release of exactly
-      // this one value.  (A release fence would also write back every dirty
-      // line of this XCD's L2 -- megabytes of map stores -- in every
-      // workgroup.)
-      __hip_atomic_store(&p.ws->partial[blockIdx.x], bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      const unsigned prev =
-          __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      is_last = (prev == (unsigned)(G - 1));
-    }
-    __syncthreads();
-    if (is_last && wave == 0) {
-      double sum = 0.0;
-      for (int k = lane; k < G; k += kWave)
-        sum += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-      if (lane == 0) {
-        *p.loss = (float)(sum * p.inv_m);
-        __hip_atomic_store(&p.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  if constexpr (MODE != kBwd) finish_loss(p, acc, red, is_last);
 }
 
 }  // namespace ssim_dev
-
-// ---------------------------------------------------------------------------
-// Entry kernels: one set per image type (named for profiles; "stream"
-// kernels mark their stores non-temporal), and the table the host launches
-// from, in KernelKind order.
-
-namespace ssim_dev {
-enum KernelKind {
-  kKFwdInfer, kKFwdTrain, kKFwdTrainStream, kKBwd, kKBwdStream, kKBwdUnaligned, kKinds
-};
-}  // namespace ssim_dev
-
-#define SSIM_ENTRY_KERNELS(T, NAME, TABLE)                                                  \
-  namespace {                                                                              \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_infer##NAME##kernel(      \
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kFwdInfer, false, false, T>(p);                          \
-  }                                                                                        \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_train##NAME##kernel(      \
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kFwdTrain, false, false, T>(p);                          \
-  }                                                                                        \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_fwd_train_stream##NAME##kernel(\
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kFwdTrain, false, true, T>(p);                           \
-  }                                                                                        \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd##NAME##kernel(            \
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kBwd, true, false, T>(p);                                \
-  }                                                                                        \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd_stream##NAME##kernel(     \
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kBwd, true, true, T>(p);                                 \
-  }                                                                                        \
-  __global__ __launch_bounds__(ssim_dev::kThreads) void ssim_bwd_unaligned##NAME##kernel(  \
-      const ssim_dev::Params p) {                                                          \
-    ssim_dev::strip_body<ssim_dev::kBwd, false, false, T>(p);                               \
-  }                                                                                        \
-  }                                                                                        \
-  const void* const* TABLE() {                                                             \
-    static const void* const t[ssim_dev::kKinds] = {                                      \
-        (const void*)ssim_fwd_infer##NAME##kernel, (const void*)ssim_fwd_train##NAME##kernel,\
-        (const void*)ssim_fwd_train_stream##NAME##kernel, (const void*)ssim_bwd##NAME##kernel,\
-        (const void*)ssim_bwd_stream##NAME##kernel,                                        \
-        (const void*)ssim_bwd_unaligned##NAME##kernel};                                    \
-    return t;                                                                              \
-  }
-
-// Kernel tables exported by the per-type translation units.
-const void* const* ssim_kernel_table_f32();
-const void* const* ssim_kernel_table_f16();
-const void* const* ssim_kernel_table_bf16();

@@ -1,0 +1,80 @@
+// ssim_entry.hpp -- the entry kernels, one set per image type, and the table
+// the host launches them from.  Each ssim_kernels_<type>.hip instantiates the
+// set for one type with SSIM_ENTRY_KERNELS; ssim_api.hip sees the KernelKind
+// order and the table accessors only.  Kernels are named for profiles:
+// "stream" kernels mark their stores non-temporal; "unaligned" kernels move
+// image elements one at a time (W not a multiple of 4, or unaligned
+// pointers).
+
+#pragma once
+
+#include "ssim_fused.hpp"
+
+namespace ssim_dev {
+enum KernelKind {
+  kKFwdInfer,          // forward, loss only
+  kKFwdTrain,          // forward, loss + saved statistics
+  kKFwdTrainStream,
+  kKBwd,               // backward from the saved statistics
+  kKBwdStream,
+  kKBwdUnaligned,
+  kKRecomp,            // backward recomputing the statistics from the images
+  kKRecompStream,
+  kKRecompUnaligned,
+  kKLossGrad,          // loss and both gradients in one pass
+  kKLossGradStream,
+  kKLossGradUnaligned,
+  kKinds
+};
+}  // namespace ssim_dev
+
+#define SSIM_KERNEL_(NAME, BODY)                                                           \
+  __global__ __launch_bounds__(ssim_dev::kThreads) void NAME(const ssim_dev::Params p) {   \
+    BODY(p);                                                                               \
+  }
+
+#define SSIM_ENTRY_KERNELS(T, NAME, TABLE)                                                  \
+  namespace {                                                                              \
+  SSIM_KERNEL_(ssim_fwd_infer##NAME##kernel,                                               \
+               (ssim_dev::strip_body<ssim_dev::kFwdInfer, false, false, T>))               \
+  SSIM_KERNEL_(ssim_fwd_train##NAME##kernel,                                               \
+               (ssim_dev::strip_body<ssim_dev::kFwdTrain, false, false, T>))               \
+  SSIM_KERNEL_(ssim_fwd_train_stream##NAME##kernel,                                        \
+               (ssim_dev::strip_body<ssim_dev::kFwdTrain, false, true, T>))                \
+  SSIM_KERNEL_(ssim_bwd##NAME##kernel, (ssim_dev::strip_body<ssim_dev::kBwd, true, false, T>)) \
+  SSIM_KERNEL_(ssim_bwd_stream##NAME##kernel,                                              \
+               (ssim_dev::strip_body<ssim_dev::kBwd, true, true, T>))                      \
+  SSIM_KERNEL_(ssim_bwd_unaligned##NAME##kernel,                                           \
+               (ssim_dev::strip_body<ssim_dev::kBwd, false, false, T>))                    \
+  SSIM_KERNEL_(ssim_bwd_recompute##NAME##kernel, (ssim_dev::fused_body<false, true, false, T>)) \
+  SSIM_KERNEL_(ssim_bwd_recompute_stream##NAME##kernel,                                    \
+               (ssim_dev::fused_body<false, true, true, T>))                               \
+  SSIM_KERNEL_(ssim_bwd_recompute_unaligned##NAME##kernel,                                 \
+               (ssim_dev::fused_body<false, false, false, T>))                             \
+  SSIM_KERNEL_(ssim_loss_grad##NAME##kernel, (ssim_dev::fused_body<true, true, false, T>))  \
+  SSIM_KERNEL_(ssim_loss_grad_stream##NAME##kernel,                                        \
+               (ssim_dev::fused_body<true, true, true, T>))                                 \
+  SSIM_KERNEL_(ssim_loss_grad_unaligned##NAME##kernel,                                     \
+               (ssim_dev::fused_body<true, false, false, T>))                              \
+  }                                                                                        \
+  const void* const* TABLE() {                                                             \
+    static const void* const t[ssim_dev::kKinds] = {                                      \
+        (const void*)ssim_fwd_infer##NAME##kernel,                                         \
+        (const void*)ssim_fwd_train##NAME##kernel,                                         \
+        (const void*)ssim_fwd_train_stream##NAME##kernel,                                  \
+        (const void*)ssim_bwd##NAME##kernel,                                               \
+        (const void*)ssim_bwd_stream##NAME##kernel,                                        \
+        (const void*)ssim_bwd_unaligned##NAME##kernel,                                     \
+        (const void*)ssim_bwd_recompute##NAME##kernel,                                     \
+        (const void*)ssim_bwd_recompute_stream##NAME##kernel,                              \
+        (const void*)ssim_bwd_recompute_unaligned##NAME##kernel,                           \
+        (const void*)ssim_loss_grad##NAME##kernel,                                         \
+        (const void*)ssim_loss_grad_stream##NAME##kernel,                                  \
+        (const void*)ssim_loss_grad_unaligned##NAME##kernel};                              \
+    return t;                                                                              \
+  }
+
+// Kernel tables exported by the per-type translation units.
+const void* const* ssim_kernel_table_f32();
+const void* const* ssim_kernel_table_f16();
+const void* const* ssim_kernel_table_bf16();

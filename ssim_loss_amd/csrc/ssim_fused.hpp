@@ -1,0 +1,343 @@
+// ssim_fused.hpp -- the recomputing kernels: image -> blurred statistics ->
+// loss partials -> adjoint blur -> gradients in one pass over the images,
+// with no map written to or read from memory.
+//
+// The gradient is the one of "TriSSIM", How it works (the adjoint B^T of the
+// blur applied to the loss partials, then the chain rule), in the basis of
+// ssim_device.hpp.  Instead of saving the blurred statistics in the forward
+// and reading them back, one kernel forms them again from the images and
+// keeps every intermediate on chip: per step it moves the images and the
+// gradients only (and, with the loss, that is the whole training step).
+//
+// Two stencil stages run in one strip of 256 lanes:
+//   stage 1 : lane t owns image column v0 - 10 + t; the column pass of the
+//             four quantities runs through a 12-slot register ring, the row
+//             pass through the LDS tile, as in the two-kernel design.  Each
+//             row-pass lane forms the SSIM terms and the four loss partials
+//             at 4 adjacent map entries and writes the partials back into the
+//             same tile row it read (zero outside the map: the adjoint's zero
+//             fill).  246 map columns feed the strip's gradients.
+//   stage 2 : lane t owns map column v0 - off2 + t; it reads its column of
+//             the partials from the tile, runs the adjoint's column pass
+//             through a second register ring, writes the result back into
+//             the same column, and the row pass gives 4 adjacent gradient
+//             entries per lane: 236 gradient columns per strip.
+// Row pipeline: image row r enters stage 1; it completes map row
+// r + off - 10, whose partials complete gradient row r - 10 in stage 2.  A
+// row range of n gradient rows therefore reads n + 20 image rows.  Map
+// entries shared by two strips or two row ranges are computed by both, and
+// the loss counts each exactly once, in the strip and range that own it.
+//
+// The tile is double-buffered per batch of 4 rows; within a batch it holds,
+// in turn, the column-blurred quantities, the partials (written over the row
+// each wave read) and the adjoint's column pass (written over the column
+// each lane read), with a barrier between the phases.
+
+#pragma once
+
+#include "ssim_device.hpp"
+
+namespace ssim_dev {
+
+constexpr int kFOut = 236;                          // gradient columns per strip
+constexpr int kFMapCols = kFOut + 10;               // map columns they need
+constexpr int kFMapLanes = (kFMapCols + 3) / 4;     // stage-1 row-pass lanes (62)
+constexpr int kFGradLanes = kFOut / 4;              // stage-2 row-pass lanes (59)
+constexpr int kFTileW = kTileW + 4;                 // 256 lanes + the last lane's 4-column overhang
+
+static_assert(kFMapCols + 10 == kTileW, "a strip's image columns are one per lane");
+static_assert(4 * (kFMapLanes - 1) + 16 <= kFTileW, "stage-1 row-pass reads stay in the tile row");
+static_assert(4 * (kFGradLanes - 1) + 16 <= 4 * kFMapLanes,
+              "stage-2 row-pass reads stay in the columns stage 1 wrote");
+static_assert(kFOut % 4 == 0 && (kFTileW * 4) % 16 == 0, "16-byte aligned tile rows and groups");
+
+struct FSeg {
+  rsrc_t img[2];        // x, y planes
+  rsrc_t out[2];        // grad_x, grad_y planes (zero-size when not wanted)
+  unsigned colbyte;     // this lane's image column (stage 1), bytes, or kOob
+  unsigned row_bytes;   // image row pitch, bytes
+  int u0, nrows;        // gradient rows [u0, u0 + nrows)
+  int v0;               // first gradient column of the strip
+  int jm0;              // first map column of the strip: v0 - off2
+  int i0;               // map row completed by the first batch row: u0 - off2
+  int own_r1;           // the loss counts map rows [i0, own_r1) ...
+  int own_c1;           // ... and map columns [jm0, own_c1) (clipped to the map)
+};
+
+// This lane's pixel of x and y in image row r (0 outside the image).
+template <int T>
+__device__ __forceinline__ void fload_row(const FSeg& s, int r, float (&v)[2]) {
+  const unsigned off = s.colbyte + (unsigned)r * s.row_bytes;
+  v[0] = ld_img<T>(s.img[0], off);
+  v[1] = ld_img<T>(s.img[1], off);
+}
+
+__device__ __forceinline__ void image_quantities(const float (&v)[2], float (&q)[kQ]) {
+  const float x = v[0] - kShift, y = v[1] - kShift;
+  const float d = v[0] - v[1];
+  q[0] = x;
+  q[1] = y;
+  q[2] = d * d;
+  q[3] = x * y;
+}
+
+// column pass of one row through a 12-slot ring: the new row goes into slot
+// (base + 10) % 12, and the output is the 11-tap sum over slots base..base+10
+template <int kBase>
+__device__ __forceinline__ void ring_column(float (&ring)[kRing][kQ], float (&cs)[kQ]) {
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) cs[q] = tap(0) * ring[kBase % kRing][q];
+#pragma unroll
+  for (int a = 1; a < 11; ++a)
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) cs[q] = __builtin_fmaf(tap(a), ring[(kBase + a) % kRing][q], cs[q]);
+}
+
+// row pass: 4 adjacent outputs of each of the 4 quantities from 16 columns of
+// a tile row starting at column c (16-byte aligned)
+__device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ][4]) {
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const float* src = row0 + q * (kRows * kFTileW) + c;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+      v[4 * k + 0] = f.x;
+      v[4 * k + 1] = f.y;
+      v[4 * k + 2] = f.z;
+      v[4 * k + 3] = f.w;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float a = tap(0) * v[u];
+#pragma unroll
+      for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
+      o[q][u] = a;
+    }
+  }
+}
+
+template <bool kLoss, bool kVec, bool kNt, int T, int PH>
+__device__ __forceinline__ void fbatch(const Params& p, const FSeg& s,
+                                       float (&tile)[2][kQ][kRows][kFTileW],
+                                       float (&ring1)[kRing][kQ], float (&ring2)[kRing][kQ],
+                                       float (&pre)[kRows][2], int t, int buf, float dl,
+                                       double& acc) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  constexpr unsigned kEb = img_bytes<T>();
+
+  // The gradient row this wave finishes in this batch, and its images for
+  // the chain rule (loaded first so their latency hides behind the batch).
+  // Memory operations are never under a branch: groups that are not real
+  // use out-of-range offsets (loads give 0, stores are dropped).
+  const int gr = 4 * t + wave - 10;  // row within the range; < 0 while stage 2 warms up
+  const bool grow = gr >= 0 && gr < s.nrows;
+  const int gv = s.v0 + 4 * lane;
+  const bool gok = grow && lane < kFGradLanes && gv < p.img_w;
+  const unsigned gbase = gok ? (unsigned)(s.u0 + gr) * s.row_bytes + (unsigned)gv * kEb : kOob;
+  unsigned goff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) goff[c] = (gok && gv + c < p.img_w) ? gbase + kEb * c : kOob;
+  float xv[4], yv[4];
+  if constexpr (kVec) {
+    ld_img4<T>(s.img[0], gbase, xv);
+    ld_img4<T>(s.img[1], gbase, yv);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      xv[c] = ld_img<T>(s.img[0], goff[c]);
+      yv[c] = ld_img<T>(s.img[1], goff[c]);
+    }
+  }
+
+  float cur[kRows][2];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    cur[m][0] = pre[m][0];
+    cur[m][1] = pre[m][1];
+  }
+  // prefetch the next batch's image rows (past the plane they read as 0)
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + 4 * (t + 1) + m, pre[m]);
+
+  // stage 1, column pass
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    constexpr int kB0 = 4 * PH;
+    float cs[kQ];
+    image_quantities(cur[m], ring1[(kB0 + m + 10) % kRing]);
+    switch (m) {  // m is a compile-time constant after unrolling
+      case 0: ring_column<kB0 + 0>(ring1, cs); break;
+      case 1: ring_column<kB0 + 1>(ring1, cs); break;
+      case 2: ring_column<kB0 + 2>(ring1, cs); break;
+      default: ring_column<kB0 + 3>(ring1, cs); break;
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
+  }
+  __syncthreads();
+
+  // stage 1, row pass: wave w -> map row i0 + 4t + w; lane l -> map columns
+  // jm0 + 4l .. 4l+3.  The partials go back into the row just read.
+  {
+    const int i = s.i0 + 4 * t + wave;
+    const bool irow = (unsigned)i < (unsigned)p.map_h;
+    const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
+    float part[kQ][4];
+    if (irow) {
+      float o[kQ][4];
+      row_pass(&tile[buf][0][wave][0], 4 * lr, o);
+      const bool own_row = kLoss && i < s.own_r1;
+      float s4 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int jl = 4 * lr + c;  // map column within the strip
+        const int jm = s.jm0 + jl;
+        const bool in_map = (unsigned)jm < (unsigned)p.map_w && jl < kFMapCols;
+        const SsimTerms st = ssim_terms(o[0][c], o[1][c], o[2][c], o[3][c]);
+        float m4[4];
+        loss_partials(o[0][c], o[1][c], st, p.k_m2, m4);
+#pragma unroll
+        for (int k = 0; k < kQ; ++k) part[k][c] = in_map ? m4[k] : 0.0f;
+        if constexpr (kLoss) {
+          const float ell = one_minus_ssim(st);
+          s4 += (own_row && in_map && lane < kFMapLanes && jm < s.own_c1) ? ell : 0.0f;
+        }
+      }
+      if constexpr (kLoss) acc += (double)s4;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kQ; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[k][c] = 0.0f;
+    }
+    if (lane < kFMapLanes) {
+#pragma unroll
+      for (int k = 0; k < kQ; ++k)
+        *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
+            make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
+    }
+  }
+  __syncthreads();
+
+  // stage 2, column pass: lane t owns map column jm0 + t; the adjoint's
+  // column-blurred rows go back into the same column
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    constexpr int kB0 = 4 * PH;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) ring2[(kB0 + m + 10) % kRing][q] = tile[buf][q][m][tid];
+    float cs[kQ];
+    switch (m) {
+      case 0: ring_column<kB0 + 0>(ring2, cs); break;
+      case 1: ring_column<kB0 + 1>(ring2, cs); break;
+      case 2: ring_column<kB0 + 2>(ring2, cs); break;
+      default: ring_column<kB0 + 3>(ring2, cs); break;
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
+  }
+  __syncthreads();
+
+  // stage 2, row pass and chain rule: wave w -> gradient row u0 + gr (the
+  // arithmetic is skipped, wave-uniformly, while stage 2 warms up)
+  float g1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (grow) {
+    const int lr = lane < kFGradLanes ? lane : kFGradLanes - 1;
+    float o[kQ][4];
+    row_pass(&tile[buf][0][wave][0], 4 * lr, o);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float xs = xv[c] - kShift, ys = yv[c] - kShift, d = xv[c] - yv[c];
+      g1[c] = dl * __builtin_fmaf(d, o[2][c], __builtin_fmaf(ys, o[3][c], o[0][c]));
+      g2[c] = dl * __builtin_fmaf(-d, o[2][c], __builtin_fmaf(xs, o[3][c], o[1][c]));
+    }
+  }
+  if constexpr (kVec) {
+    st_img4<T, kNt>(s.out[0], gbase, g1);
+    st_img4<T, kNt>(s.out[1], gbase, g2);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st_img<T, kNt>(s.out[0], goff[c], g1[c]);
+      st_img<T, kNt>(s.out[1], goff[c], g2[c]);
+    }
+  }
+}
+
+// kLoss: also form loss = 1 - mean SSIM (the whole training step in one
+// launch); otherwise gradients only (a backward that needs no saved maps).
+template <bool kLoss, bool kVec, bool kNt, int T>
+__device__ __forceinline__ void fused_body(const Params& p) {
+  __shared__ float tile[2][kQ][kRows][kFTileW];
+  __shared__ double red[kWaves];
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x;
+  const Share w = work_share(p, p.out_h);  // gradient rows
+  const float dl = *p.dloss;
+  constexpr unsigned kEb = img_bytes<T>();
+
+  double acc = 0.0;
+  int buf = 0;
+  for (int64_t sc = w.sc_begin; sc < w.sc_end; ++sc) {
+    FSeg s;
+    const int64_t plane = sc / p.strips;
+    const int strip = (int)(sc - plane * p.strips);
+    s.u0 = w.row_begin;
+    s.nrows = w.row_end - w.row_begin;
+    s.v0 = strip * kFOut;
+    s.jm0 = s.v0 - p.off2;
+    s.i0 = s.u0 - p.off2;
+    const int c = s.v0 - 10 + tid;
+    s.colbyte = (c >= 0 && c < p.img_w) ? (unsigned)c * kEb : kOob;
+    s.row_bytes = (unsigned)p.img_w * kEb;
+    const int64_t pb = plane * p.img_plane * kEb;
+    s.img[0] = make_rsrc(byte_ptr(p.x, pb), p.img_plane * kEb);
+    s.img[1] = make_rsrc(byte_ptr(p.y, pb), p.img_plane * kEb);
+    s.out[0] = make_rsrc(p.gx ? byte_ptr(p.gx, pb) : p.x, p.gx ? p.img_plane * kEb : 0);
+    s.out[1] = make_rsrc(p.gy ? byte_ptr(p.gy, pb) : p.y, p.gy ? p.img_plane * kEb : 0);
+    // the last row range and the last strip own the map's remaining rows and
+    // columns (same padding: the map reaches 5 past the last gradient row
+    // range's own share)
+    s.own_r1 = (w.row_end == p.out_h) ? p.map_h : w.row_end - p.off2;
+    s.own_c1 = (strip == p.strips - 1) ? p.map_w : s.jm0 + kFOut;
+    const int nb = (s.nrows + 10 + kRows - 1) / kRows;
+
+    float ring1[kRing][kQ];
+    float ring2[kRing][kQ];
+    float pre[kRows][2];
+    {
+      float warm[10][2];
+#pragma unroll
+      for (int k = 0; k < 10; ++k) fload_row<T>(s, s.u0 - 10 + k, warm[k]);
+#pragma unroll
+      for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + m, pre[m]);
+#pragma unroll
+      for (int k = 0; k < 10; ++k) image_quantities(warm[k], ring1[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRing; ++k)
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) ring2[k][q] = 0.0f;
+
+    for (int t = 0;;) {
+      if (t >= nb) break;
+      fbatch<kLoss, kVec, kNt, T, 0>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
+      buf ^= 1;
+      if (++t >= nb) break;
+      fbatch<kLoss, kVec, kNt, T, 1>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
+      buf ^= 1;
+      if (++t >= nb) break;
+      fbatch<kLoss, kVec, kNt, T, 2>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
+      buf ^= 1;
+      ++t;
+    }
+  }
+  if constexpr (kLoss) finish_loss(p, acc, red, is_last);
+}
+
+}  // namespace ssim_dev

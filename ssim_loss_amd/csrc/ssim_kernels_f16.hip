@@ -1,5 +1,5 @@
 // Entry kernels of the fused SSIM loss for fp16 images and gradients (the
-// arithmetic is fp32 throughout; see ssim_device.hpp).
-#include "ssim_device.hpp"
+// arithmetic is fp32 throughout; see ssim_device.hpp and ssim_fused.hpp).
+#include "ssim_entry.hpp"
 
 SSIM_ENTRY_KERNELS(ssim_dev::kImgF16, _f16_, ssim_kernel_table_f16)

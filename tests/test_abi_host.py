@@ -24,6 +24,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["ssim_forward", "ssim_backward", "ssim_forward_typed", "ssim_backward_typed",
+              "ssim_backward_recompute", "ssim_loss_and_grad",
               "ssim_saved_maps_bytes", "ssim_workspace_bytes", "ssim_strerror",
               "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
         assert n in names
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert S.ssim_abi_version() == 2
+    assert S.ssim_abi_version() == 3
     for code in range(0, -9, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
@@ -132,6 +133,46 @@ def test_typed_overlap_uses_element_size():
     assert lib.ssim_forward_typed(0x10000, 0x100000, 1, 1, 1, 64, 64, 0, 0x10000 + 4096,
                                   None, 0x900000, None) == -5
     assert S.ssim_strerror(-8)
+
+
+def _rec(lib, dloss=0x1000, img1=0x10000, img2=0x100000, dt=0, N=1, C=1, H=64, W=64, padding=0,
+         g1=0x900000, g2=0xA00000):
+    return lib.ssim_backward_recompute(dloss, img1, img2, dt, N, C, H, W, padding, g1, g2, None)
+
+
+def _lag(lib, img1=0x10000, img2=0x100000, dt=0, N=1, C=1, H=64, W=64, padding=0, dloss=0x1000,
+         loss=0x2000, ws=0x300000, g1=0x900000, g2=0xA00000):
+    return lib.ssim_loss_and_grad(img1, img2, dt, N, C, H, W, padding, dloss, loss, ws, g1, g2,
+                                  None)
+
+
+def test_recompute_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    assert _rec(lib, dloss=None) == -1
+    assert _rec(lib, img1=None) == -1
+    assert _rec(lib, dt=5) == -8
+    assert _rec(lib, padding=3) == -3
+    assert _rec(lib, H=10) == -2
+    assert _rec(lib, img2=0x100002) == -2           # fp32 image not 4-byte aligned
+    assert _rec(lib, dt=1, g1=0x900001) == -2       # fp16 gradient not 2-byte aligned
+    assert _rec(lib, g1=0x10000 + 64) == -5         # gradient inside img1
+    assert _rec(lib, g2=0x900000 + 4) == -5         # gradients overlap
+    assert _rec(lib, g1=0x1000 - 8) == -5           # gradient covers dloss
+    assert _rec(lib, H=1 << 14, W=(1 << 13) + 4) == -4
+    assert _rec(lib, g1=None, g2=None) == 0         # nothing to do: no launch
+
+
+def test_loss_and_grad_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    assert _lag(lib, loss=None) == -1
+    assert _lag(lib, ws=None) == -1
+    assert _lag(lib, dloss=None) == -1
+    assert _lag(lib, dt=-1) == -8
+    assert _lag(lib, padding=9) == -3
+    assert _lag(lib, W=0) == -2
+    assert _lag(lib, loss=0x100000 + 16) == -5      # loss inside img2
+    assert _lag(lib, ws=0x900000 + 4096) == -5      # workspace overlaps a gradient
+    assert _lag(lib, loss=0x300000 + 8) == -5       # loss inside the workspace
 
 
 def test_python_binding_rejects_cpu_tensors():
