@@ -3,11 +3,12 @@
 One step = one forward + backward of the chosen design (--design) on one batch
 of synthetic images already resident in HBM, through the C ABI on torch's
 current stream:
+  one-pass  : ssim_loss_and_grad (loss and both gradients in one launch;
+              the default)
   saved     : ssim_forward (training mode: loss + saved maps), then
               ssim_backward (both image gradients)
   recompute : ssim_forward (inference: loss only), then
               ssim_backward_recompute (both gradients, no maps)
-  one-pass  : ssim_loss_and_grad (loss and both gradients in one launch)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--dtype float32|float16|bfloat16] [--design NAME] [--all-kernels]
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (256 CUs, 2.4 GHz)
 PAGES_MPIX_S = 1920 * 1080 / 7.2e-3 / 1e6  # the pages' 7.2 ms fwd+bwd at 1080p (RDNA4 R9700)
 CSRC = os.path.join(ROOT, "ssim_loss_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -45,7 +47,7 @@ def parse():
     ap.add_argument("--workload", default="1080p-valid")
     ap.add_argument("--dtype", default="float32", choices=["float32", "float16", "bfloat16"],
                     help="storage type of images and gradients (arithmetic is fp32)")
-    ap.add_argument("--design", default="saved", choices=["saved", "recompute", "one-pass"],
+    ap.add_argument("--design", default="one-pass", choices=["saved", "recompute", "one-pass"],
                     help="saved: forward saves the statistics, backward reads them; "
                          "recompute: loss-only forward, backward recomputes the statistics; "
                          "one-pass: loss and gradients in one launch")
@@ -84,6 +86,28 @@ def algorithmic_bytes(shape, padding, eb=4):
             "ssim_forward(inference)": 2 * eb * e_in,
             "ssim_backward_recompute": 4 * eb * e_in,
             "ssim_loss_and_grad": 4 * eb * e_in}
+
+
+def algorithmic_flops(shape, padding):
+    """fp32 operations per launch of each kernel (a fused multiply-add counts
+    2), from the arithmetic of the method in the kernels' basis: per image
+    element 5 for the products x', y', x - y, (x - y)^2, x'y'; per blurred
+    quantity and output, 21 per separable pass (one multiply, ten FMAs) in
+    each direction; per map entry 17 for the SSIM terms, 5 for 1 - S and its
+    sum, 25 for the four loss partials; per image element 13 for the chain
+    rule.  Four quantities are blurred forward (to map entries) and four
+    partials backward (to image elements)."""
+    N, C, H, W = shape
+    Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
+    e_in = N * C * H * W
+    e_out = N * C * Ho * Wo
+    blur = 4 * 2 * 21
+    fwd = 5 * e_in + (blur + 17 + 5) * e_out
+    bwd_from_stats = (17 + 25) * e_out + (blur + 13) * e_in
+    recompute = 5 * e_in + (blur + 17 + 25) * e_out + (blur + 13) * e_in
+    return {"ssim_forward": fwd, "ssim_forward(inference)": fwd,
+            "ssim_backward": bwd_from_stats, "ssim_backward_recompute": recompute,
+            "ssim_loss_and_grad": recompute + 5 * e_out}
 
 
 def cpu_baseline(x, y, padding, pixels_per_image_batch):
@@ -228,8 +252,14 @@ def main():
         torch.cuda.synchronize()
 
     alg = algorithmic_bytes((N, C, H, W), w.padding, eb)
+    flops = algorithmic_flops((N, C, H, W), w.padding)
     dom = max(DESIGNS[args.design], key=lambda k: kern[k])
     achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
+    achieved_tf = flops[dom] / (kern[dom] * 1e-3) / 1e12
+    # the bound of the dominant kernel: the resource it uses the larger
+    # fraction of (the saved-maps kernels stream HBM; the recomputing ones
+    # are arithmetic-heavy)
+    alu_bound = achieved_tf / FP32_VECTOR_PEAK_TFLOPS > achieved / HBM_PEAK_GBS
 
     # HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
     # WRITE_SIZE, scaled by a copy kernel of known size), valid only for the
@@ -252,9 +282,11 @@ def main():
         if all(k in kern for k in ks):
             ms = sum(kern[k] for k in ks)
             by = sum(alg[k] for k in ks)
+            fl = sum(flops[k] for k in ks)
             designs[d] = {"ms_per_step": round(ms, 5), "mpix_per_s": round(mpix / (ms * 1e-3), 1),
                           "hbm_bytes_per_elem": round(by / (N * C * H * W), 2),
-                          "algorithmic_gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+                          "algorithmic_gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                          "algorithmic_tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
 
     out = {
         "metric": "Mpix/s fused SSIM fwd+bwd fp32 at 1080p; achieved HBM GB/s as % of peak",
@@ -273,7 +305,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "shape": [N, C, H, W], "padding": w.padding,
                    "design": args.design},
-        "roofline": {
+        "roofline": ({
+            "bound": "alu",
+            "kernel": dom,
+            "achieved": round(achieved_tf, 2),
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops": flops[dom],
+            "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg[dom]},
+        } if alu_bound else {
             "bound": "hbm",
             "kernel": dom,
             "achieved": round(achieved, 1),
@@ -282,7 +325,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": alg[dom],
-        },
+            "alu": {"achieved": round(achieved_tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                    "algorithmic_flops": flops[dom]},
+        }),
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "designs": designs,
         "cold": cold,

@@ -16,9 +16,10 @@ are called for the half types):
   ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
   ssim_strerror, ssim_abi_version
 Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
-  ssim_loss(img1, img2, padding="valid", train=True, recompute=False)
-      -> 1 - mean SSIM; recompute=True keeps no maps between forward and
-         backward (the backward forms the statistics again from the images)
+  ssim_loss(img1, img2, padding="valid", train=True, recompute=True)
+      -> 1 - mean SSIM; by default no maps are kept between forward and
+         backward (the backward forms the statistics again from the images);
+         recompute=False saves them
   fused_ssim(img1, img2, padding="same", train=True)  -> mean SSIM
 One-pass step, for an upstream gradient known in advance:
   loss_and_grad(img1, img2, padding="valid", weight=1.0)
@@ -314,11 +315,14 @@ def _make_function():
 _fn = None
 
 
-def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute: bool = False):
+def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute: bool = True):
     """loss = 1 - mean SSIM (a 0-d fp32 tensor on the images' device), with
-    gradients for whichever of img1 / img2 requires them.  recompute=True
-    saves no maps for the backward (16 bytes per map entry less memory) and
-    forms the statistics again from the images when the gradient is taken."""
+    gradients for whichever of img1 / img2 requires them.  With recompute
+    (the default) the forward saves nothing but the images and the backward
+    forms the statistics again from them; recompute=False saves the four
+    blurred statistics (16 bytes per map entry) for the backward to read.
+    Both give the same gradient; the recomputing backward is as fast at 1080p
+    and faster on larger batches."""
     global _fn
     if _fn is None:
         _fn = _make_function()

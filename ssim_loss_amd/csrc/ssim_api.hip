@@ -60,7 +60,7 @@ int device_info(const DeviceInfo** out) {
       for (int t = 0; t < kTypes; ++t)
         for (int k = 0; k < kKinds; ++k) {
           int n = 0;
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_table(t)[k], kThreads, 0) !=
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_table(t)[k], kind_threads(k), 0) !=
               hipSuccess)
             return SSIM_ERR_HIP;
           d.occ[t][k] = n > 0 ? n : 1;
@@ -263,8 +263,8 @@ int backward_impl(const float* dloss, const void* img1, const void* img2, int dt
 
 // The recomputing kernels read only the images: the backward without saved
 // maps (loss == NULL) and the one-pass loss and gradients (loss != NULL).
-// A row range of n gradient rows reads n + 20 image rows, so ranges are kept
-// at least kRecompMinRows long.
+// A run of n gradient rows of one strip-column reads n + 20 image rows, so
+// each workgroup gets at least kRecompMinRows rows.
 constexpr int kRecompMinRows = 40;
 
 int recompute_impl(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
@@ -328,7 +328,19 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   const bool stream_st = 4 * s.img_bytes > kStreamBytes;
   const int which = loss ? (!vec ? kKLossGradUnaligned : stream_st ? kKLossGradStream : kKLossGrad)
                          : (!vec ? kKRecompUnaligned : stream_st ? kKRecompStream : kKRecomp);
-  return launch(d, dtype, which, p, stream, kRecompMinRows);
+  // one resident wave of workgroups, each with an equal run of (strip-column,
+  // row) pairs, and at least kRecompMinRows rows each
+  const int64_t rows = p.cols * (int64_t)p.out_h;
+  int64_t G = (int64_t)d->cus * d->occ[dtype][which];
+  if (G > kMaxBlocks) G = kMaxBlocks;
+  const int64_t by_rows = (rows + kRecompMinRows - 1) / kRecompMinRows;
+  if (G > by_rows) G = by_rows;
+  if (G < 1) G = 1;
+  void* args[] = {&p};
+  if (hipLaunchKernel(kernel_table(dtype)[which], dim3((unsigned)G), dim3(kind_threads(which)), args,
+                      0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSIM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
 }  // namespace

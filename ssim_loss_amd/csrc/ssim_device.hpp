@@ -558,7 +558,8 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
 
 // Workgroup sum of the map of 1 - S, then the last workgroup to finish
 // forms the mean: loss = sum / M.  Every thread of the workgroup calls it.
-__device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kWaves],
+template <int kNW>
+__device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kNW],
                                             int& is_last) {
   const int tid = threadIdx.x;
   const int G = gridDim.x;
@@ -570,7 +571,7 @@ __device__ __forceinline__ void finish_loss(const Params& p, double acc, double 
   if (tid == 0) {
     double bs = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) bs += red[w];
+    for (int w = 0; w < kNW; ++w) bs += red[w];
     // Publish the partial with a device-coherent atomic store and wait for
     // its acknowledgement before taking the ticket: a release of exactly
     // this one value.  (A release fence would also write back every dirty
@@ -605,10 +606,15 @@ struct Share {
   int row_begin, row_end;
 };
 
-__device__ __forceinline__ Share work_share(const Params& p, int rows) {
+__device__ __forceinline__ int logical_block() {
   const int G = gridDim.x;
   int lb = blockIdx.x;
   if ((G & 7) == 0) lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  return lb;
+}
+
+__device__ __forceinline__ Share work_share(const Params& p, int rows) {
+  const int lb = logical_block();
   Share w;
   if (p.parts > 1) {
     w.sc_begin = lb / p.parts;
@@ -705,7 +711,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     }
   }
 
-  if constexpr (MODE != kBwd) finish_loss(p, acc, red, is_last);
+  if constexpr (MODE != kBwd) finish_loss<kWaves>(p, acc, red, is_last);
 }
 
 }  // namespace ssim_dev

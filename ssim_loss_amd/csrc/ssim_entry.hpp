@@ -11,6 +11,8 @@
 #include "ssim_fused.hpp"
 
 namespace ssim_dev {
+// threads per workgroup of each kernel kind: the recomputing kernels run two
+// groups of 4 waves (one per stencil stage)
 enum KernelKind {
   kKFwdInfer,          // forward, loss only
   kKFwdTrain,          // forward, loss + saved statistics
@@ -26,10 +28,15 @@ enum KernelKind {
   kKLossGradUnaligned,
   kKinds
 };
+__host__ __device__ constexpr int kind_threads(int k) { return k >= kKRecomp ? kFThreads : kThreads; }
 }  // namespace ssim_dev
 
 #define SSIM_KERNEL_(NAME, BODY)                                                           \
   __global__ __launch_bounds__(ssim_dev::kThreads) void NAME(const ssim_dev::Params p) {   \
+    BODY(p);                                                                               \
+  }
+#define SSIM_FKERNEL_(NAME, BODY)                                                          \
+  __global__ __launch_bounds__(ssim_dev::kFThreads) void NAME(const ssim_dev::Params p) {  \
     BODY(p);                                                                               \
   }
 
@@ -46,15 +53,15 @@ enum KernelKind {
                (ssim_dev::strip_body<ssim_dev::kBwd, true, true, T>))                      \
   SSIM_KERNEL_(ssim_bwd_unaligned##NAME##kernel,                                           \
                (ssim_dev::strip_body<ssim_dev::kBwd, false, false, T>))                    \
-  SSIM_KERNEL_(ssim_bwd_recompute##NAME##kernel, (ssim_dev::fused_body<false, true, false, T>)) \
-  SSIM_KERNEL_(ssim_bwd_recompute_stream##NAME##kernel,                                    \
+  SSIM_FKERNEL_(ssim_bwd_recompute##NAME##kernel, (ssim_dev::fused_body<false, true, false, T>)) \
+  SSIM_FKERNEL_(ssim_bwd_recompute_stream##NAME##kernel,                                    \
                (ssim_dev::fused_body<false, true, true, T>))                               \
-  SSIM_KERNEL_(ssim_bwd_recompute_unaligned##NAME##kernel,                                 \
+  SSIM_FKERNEL_(ssim_bwd_recompute_unaligned##NAME##kernel,                                 \
                (ssim_dev::fused_body<false, false, false, T>))                             \
-  SSIM_KERNEL_(ssim_loss_grad##NAME##kernel, (ssim_dev::fused_body<true, true, false, T>))  \
-  SSIM_KERNEL_(ssim_loss_grad_stream##NAME##kernel,                                        \
+  SSIM_FKERNEL_(ssim_loss_grad##NAME##kernel, (ssim_dev::fused_body<true, true, false, T>))  \
+  SSIM_FKERNEL_(ssim_loss_grad_stream##NAME##kernel,                                        \
                (ssim_dev::fused_body<true, true, true, T>))                                 \
-  SSIM_KERNEL_(ssim_loss_grad_unaligned##NAME##kernel,                                     \
+  SSIM_FKERNEL_(ssim_loss_grad_unaligned##NAME##kernel,                                     \
                (ssim_dev::fused_body<true, false, false, T>))                              \
   }                                                                                        \
   const void* const* TABLE() {                                                             \

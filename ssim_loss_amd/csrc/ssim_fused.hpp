@@ -44,6 +44,8 @@ constexpr int kFMapCols = kFOut + 10;               // map columns they need
 constexpr int kFMapLanes = (kFMapCols + 3) / 4;     // stage-1 row-pass lanes (62)
 constexpr int kFGradLanes = kFOut / 4;              // stage-2 row-pass lanes (59)
 constexpr int kFTileW = kTileW + 4;                 // 256 lanes + the last lane's 4-column overhang
+constexpr int kFThreads = 2 * kThreads;             // two groups of 4 waves, one per stage
+constexpr int kFWaves = kFThreads / kWave;
 
 static_assert(kFMapCols + 10 == kTileW, "a strip's image columns are one per lane");
 static_assert(4 * (kFMapLanes - 1) + 16 <= kFTileW, "stage-1 row-pass reads stay in the tile row");
@@ -118,22 +120,98 @@ __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ
   }
 }
 
-template <bool kLoss, bool kVec, bool kNt, int T, int PH>
-__device__ __forceinline__ void fbatch(const Params& p, const FSeg& s,
-                                       float (&tile)[2][kQ][kRows][kFTileW],
-                                       float (&ring1)[kRing][kQ], float (&ring2)[kRing][kQ],
-                                       float (&pre)[kRows][2], int t, int buf, float dl,
-                                       double& acc) {
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-  constexpr unsigned kEb = img_bytes<T>();
+// Stage 1 of batch t (PH = t mod 3): the column pass of image rows u0 + 4t
+// .. +3 into the tile, then the row pass of tile row `wave` -> SSIM terms,
+// loss and partials, written back over that row.  Two barriers.
+template <bool kLoss, int T, int PH>
+__device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
+                                             float (&tile)[2][kQ][kRows][kFTileW],
+                                             float (&ring)[kRing][kQ], float (&pre)[kRows][2],
+                                             int t, int buf, int col, int wave, int lane,
+                                             double& acc) {
+  float cur[kRows][2];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    cur[m][0] = pre[m][0];
+    cur[m][1] = pre[m][1];
+  }
+  // prefetch the next batch's image rows (past the plane they read as 0)
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + 4 * (t + 1) + m, pre[m]);
 
-  // The gradient row this wave finishes in this batch, and its images for
-  // the chain rule (loaded first so their latency hides behind the batch).
-  // Memory operations are never under a branch: groups that are not real
-  // use out-of-range offsets (loads give 0, stores are dropped).
-  const int gr = 4 * t + wave - 10;  // row within the range; < 0 while stage 2 warms up
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    constexpr int kB0 = 4 * PH;
+    float cs[kQ];
+    image_quantities(cur[m], ring[(kB0 + m + 10) % kRing]);
+    switch (m) {  // m is a compile-time constant after unrolling
+      case 0: ring_column<kB0 + 0>(ring, cs); break;
+      case 1: ring_column<kB0 + 1>(ring, cs); break;
+      case 2: ring_column<kB0 + 2>(ring, cs); break;
+      default: ring_column<kB0 + 3>(ring, cs); break;
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) tile[buf][q][m][col] = cs[q];
+  }
+  __syncthreads();
+
+  // row pass: wave w -> map row i0 + 4t + w; lane l -> map columns
+  // jm0 + 4l .. 4l+3.  The partials go back into the row just read.
+  const int i = s.i0 + 4 * t + wave;
+  const bool irow = (unsigned)i < (unsigned)p.map_h;
+  const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
+  float part[kQ][4];
+  if (irow) {
+    float o[kQ][4];
+    row_pass(&tile[buf][0][wave][0], 4 * lr, o);
+    const bool own_row = kLoss && i < s.own_r1;
+    float s4 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int jl = 4 * lr + c;  // map column within the strip
+      const int jm = s.jm0 + jl;
+      const bool in_map = (unsigned)jm < (unsigned)p.map_w && jl < kFMapCols;
+      const SsimTerms st = ssim_terms(o[0][c], o[1][c], o[2][c], o[3][c]);
+      float m4[4];
+      loss_partials(o[0][c], o[1][c], st, p.k_m2, m4);
+#pragma unroll
+      for (int k = 0; k < kQ; ++k) part[k][c] = in_map ? m4[k] : 0.0f;
+      if constexpr (kLoss) {
+        const float ell = one_minus_ssim(st);
+        s4 += (own_row && in_map && lane < kFMapLanes && jm < s.own_c1) ? ell : 0.0f;
+      }
+    }
+    if constexpr (kLoss) acc += (double)s4;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kQ; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) part[k][c] = 0.0f;
+  }
+  if (lane < kFMapLanes) {
+#pragma unroll
+    for (int k = 0; k < kQ; ++k)
+      *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
+          make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
+  }
+  __syncthreads();
+}
+
+// Stage 2 of batch t: the adjoint's column pass over the partials stage 1
+// left in the tile (lane t owns map column jm0 + t; written back into the
+// same column), then the row pass of tile row `wave` and the chain rule for
+// gradient row u0 + 4t + wave - 10.  Two barriers.
+template <bool kVec, bool kNt, int T, int PH>
+__device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
+                                             float (&tile)[2][kQ][kRows][kFTileW],
+                                             float (&ring)[kRing][kQ], int t, int buf, int col,
+                                             int wave, int lane, float dl) {
+  constexpr unsigned kEb = img_bytes<T>();
+  // the gradient row this wave finishes, and its images for the chain rule
+  // (loaded first, so their latency hides behind the column pass).  Memory
+  // operations are never under a branch: groups that are not real use
+  // out-of-range offsets (loads give 0, stores are dropped).
+  const int gr = 4 * t + wave - 10;  // row within the range; < 0 while the adjoint warms up
   const bool grow = gr >= 0 && gr < s.nrows;
   const int gv = s.v0 + 4 * lane;
   const bool gok = grow && lane < kFGradLanes && gv < p.img_w;
@@ -153,97 +231,24 @@ __device__ __forceinline__ void fbatch(const Params& p, const FSeg& s,
     }
   }
 
-  float cur[kRows][2];
-#pragma unroll
-  for (int m = 0; m < kRows; ++m) {
-    cur[m][0] = pre[m][0];
-    cur[m][1] = pre[m][1];
-  }
-  // prefetch the next batch's image rows (past the plane they read as 0)
-#pragma unroll
-  for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + 4 * (t + 1) + m, pre[m]);
-
-  // stage 1, column pass
-#pragma unroll
-  for (int m = 0; m < kRows; ++m) {
-    constexpr int kB0 = 4 * PH;
-    float cs[kQ];
-    image_quantities(cur[m], ring1[(kB0 + m + 10) % kRing]);
-    switch (m) {  // m is a compile-time constant after unrolling
-      case 0: ring_column<kB0 + 0>(ring1, cs); break;
-      case 1: ring_column<kB0 + 1>(ring1, cs); break;
-      case 2: ring_column<kB0 + 2>(ring1, cs); break;
-      default: ring_column<kB0 + 3>(ring1, cs); break;
-    }
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
-  }
-  __syncthreads();
-
-  // stage 1, row pass: wave w -> map row i0 + 4t + w; lane l -> map columns
-  // jm0 + 4l .. 4l+3.  The partials go back into the row just read.
-  {
-    const int i = s.i0 + 4 * t + wave;
-    const bool irow = (unsigned)i < (unsigned)p.map_h;
-    const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
-    float part[kQ][4];
-    if (irow) {
-      float o[kQ][4];
-      row_pass(&tile[buf][0][wave][0], 4 * lr, o);
-      const bool own_row = kLoss && i < s.own_r1;
-      float s4 = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int jl = 4 * lr + c;  // map column within the strip
-        const int jm = s.jm0 + jl;
-        const bool in_map = (unsigned)jm < (unsigned)p.map_w && jl < kFMapCols;
-        const SsimTerms st = ssim_terms(o[0][c], o[1][c], o[2][c], o[3][c]);
-        float m4[4];
-        loss_partials(o[0][c], o[1][c], st, p.k_m2, m4);
-#pragma unroll
-        for (int k = 0; k < kQ; ++k) part[k][c] = in_map ? m4[k] : 0.0f;
-        if constexpr (kLoss) {
-          const float ell = one_minus_ssim(st);
-          s4 += (own_row && in_map && lane < kFMapLanes && jm < s.own_c1) ? ell : 0.0f;
-        }
-      }
-      if constexpr (kLoss) acc += (double)s4;
-    } else {
-#pragma unroll
-      for (int k = 0; k < kQ; ++k)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) part[k][c] = 0.0f;
-    }
-    if (lane < kFMapLanes) {
-#pragma unroll
-      for (int k = 0; k < kQ; ++k)
-        *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
-            make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
-    }
-  }
-  __syncthreads();
-
-  // stage 2, column pass: lane t owns map column jm0 + t; the adjoint's
-  // column-blurred rows go back into the same column
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
     constexpr int kB0 = 4 * PH;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) ring2[(kB0 + m + 10) % kRing][q] = tile[buf][q][m][tid];
+    for (int q = 0; q < kQ; ++q) ring[(kB0 + m + 10) % kRing][q] = tile[buf][q][m][col];
     float cs[kQ];
     switch (m) {
-      case 0: ring_column<kB0 + 0>(ring2, cs); break;
-      case 1: ring_column<kB0 + 1>(ring2, cs); break;
-      case 2: ring_column<kB0 + 2>(ring2, cs); break;
-      default: ring_column<kB0 + 3>(ring2, cs); break;
+      case 0: ring_column<kB0 + 0>(ring, cs); break;
+      case 1: ring_column<kB0 + 1>(ring, cs); break;
+      case 2: ring_column<kB0 + 2>(ring, cs); break;
+      default: ring_column<kB0 + 3>(ring, cs); break;
     }
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
+    for (int q = 0; q < kQ; ++q) tile[buf][q][m][col] = cs[q];
   }
   __syncthreads();
 
-  // stage 2, row pass and chain rule: wave w -> gradient row u0 + gr (the
-  // arithmetic is skipped, wave-uniformly, while stage 2 warms up)
+  // the arithmetic is skipped, wave-uniformly, while the adjoint warms up
   float g1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (grow) {
     const int lr = lane < kFGradLanes ? lane : kFGradLanes - 1;
@@ -266,33 +271,52 @@ __device__ __forceinline__ void fbatch(const Params& p, const FSeg& s,
       st_img<T, kNt>(s.out[1], goff[c], g2[c]);
     }
   }
+  __syncthreads();
 }
 
-// kLoss: also form loss = 1 - mean SSIM (the whole training step in one
-// launch); otherwise gradients only (a backward that needs no saved maps).
-template <bool kLoss, bool kVec, bool kNt, int T>
-__device__ __forceinline__ void fused_body(const Params& p) {
-  __shared__ float tile[2][kQ][kRows][kFTileW];
-  __shared__ double red[kWaves];
-  __shared__ int is_last;
+// This workgroup's share: an equal contiguous run of a sequence in which
+// each strip-column counts as its kWarm warm-up rows followed by its
+// gradient rows, so a share that starts a strip-column is charged for the
+// warm-up it pays; a share that starts inside one pays at most kWarm more.
+// The share is taken as one segment per strip-column it touches.
+struct FShare {
+  int64_t v, v_end, vlen;
+};
+constexpr int kWarm = 20;
 
-  const int tid = threadIdx.x;
-  const Share w = work_share(p, p.out_h);  // gradient rows
-  const float dl = *p.dloss;
+__device__ __forceinline__ FShare fused_share(const Params& p) {
+  FShare w;
+  w.vlen = (int64_t)p.out_h + kWarm;
+  const int64_t total = p.cols * w.vlen;
+  const int64_t lb = logical_block();
+  w.v = lb * total / gridDim.x;
+  w.v_end = (lb + 1) * total / gridDim.x;
+  return w;
+}
+
+// The next segment of the share: false when the share is done.  A segment
+// with no gradient rows (a share's tail inside a warm-up) is skipped.
+template <int T>
+__device__ __forceinline__ bool next_segment(const Params& p, FShare& w, FSeg& s, int col) {
   constexpr unsigned kEb = img_bytes<T>();
-
-  double acc = 0.0;
-  int buf = 0;
-  for (int64_t sc = w.sc_begin; sc < w.sc_end; ++sc) {
-    FSeg s;
+  for (;;) {
+    if (w.v >= w.v_end) return false;
+    const int64_t sc = w.v / w.vlen;
+    const int64_t col_end = (sc + 1) * w.vlen;
+    const int64_t seg_end = col_end < w.v_end ? col_end : w.v_end;
+    const int64_t r0 = w.v - sc * w.vlen - kWarm, r1 = seg_end - sc * w.vlen - kWarm;
+    const int row_begin = (int)(r0 > 0 ? r0 : 0);
+    const int row_end = (int)(r1 > 0 ? r1 : 0);
+    w.v = seg_end;
+    if (row_end <= row_begin) continue;
     const int64_t plane = sc / p.strips;
     const int strip = (int)(sc - plane * p.strips);
-    s.u0 = w.row_begin;
-    s.nrows = w.row_end - w.row_begin;
+    s.u0 = row_begin;
+    s.nrows = row_end - row_begin;
     s.v0 = strip * kFOut;
     s.jm0 = s.v0 - p.off2;
     s.i0 = s.u0 - p.off2;
-    const int c = s.v0 - 10 + tid;
+    const int c = s.v0 - 10 + col;
     s.colbyte = (c >= 0 && c < p.img_w) ? (unsigned)c * kEb : kOob;
     s.row_bytes = (unsigned)p.img_w * kEb;
     const int64_t pb = plane * p.img_plane * kEb;
@@ -303,41 +327,100 @@ __device__ __forceinline__ void fused_body(const Params& p) {
     // the last row range and the last strip own the map's remaining rows and
     // columns (same padding: the map reaches 5 past the last gradient row
     // range's own share)
-    s.own_r1 = (w.row_end == p.out_h) ? p.map_h : w.row_end - p.off2;
+    s.own_r1 = (row_end == p.out_h) ? p.map_h : row_end - p.off2;
     s.own_c1 = (strip == p.strips - 1) ? p.map_w : s.jm0 + kFOut;
-    const int nb = (s.nrows + 10 + kRows - 1) / kRows;
+    return true;
+  }
+}
 
-    float ring1[kRing][kQ];
-    float ring2[kRing][kQ];
-    float pre[kRows][2];
-    {
-      float warm[10][2];
+// batches of a segment: n gradient rows need n + 10 rows of partials
+__device__ __forceinline__ int segment_batches(const FSeg& s) {
+  return (s.nrows + 10 + kRows - 1) / kRows;
+}
+
+// kLoss: also form loss = 1 - mean SSIM (the whole training step in one
+// launch); otherwise gradients only (a backward that needs no saved maps).
+//
+// Eight waves: waves 0-3 run stage 1 on batch t while waves 4-7 run stage 2
+// on batch t-1, so each wave holds one register ring and the workgroup keeps
+// more waves resident per SIMD.  Batch t lives in tile buffer (number of
+// batches before it in this workgroup) mod 2; per segment each group passes
+// 2 (nb + 1) barriers (stage 2 idles through the first tick, stage 1
+// through the last), so the two loops meet at every barrier.
+template <bool kLoss, bool kVec, bool kNt, int T>
+__device__ __forceinline__ void fused_body(const Params& p) {
+  __shared__ float tile[2][kQ][kRows][kFTileW];
+  __shared__ double red[kFWaves];
+  __shared__ int is_last;
+
+  // wave index as a scalar, so the split below is a scalar branch: each wave
+  // runs exactly one of the two loops
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  FShare w = fused_share(p);
+  double acc = 0.0;
+  int gb = 0;  // batches of earlier segments
+
+  if (wave_id < kWaves) {
+    // stage 1
+    const int col = threadIdx.x;
+    FSeg s;
+    while (next_segment<T>(p, w, s, col)) {
+      const int nb = segment_batches(s);
+      float ring[kRing][kQ];
+      float pre[kRows][2];
+      {
+        float warm[10][2];
 #pragma unroll
-      for (int k = 0; k < 10; ++k) fload_row<T>(s, s.u0 - 10 + k, warm[k]);
+        for (int k = 0; k < 10; ++k) fload_row<T>(s, s.u0 - 10 + k, warm[k]);
 #pragma unroll
-      for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + m, pre[m]);
+        for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + m, pre[m]);
 #pragma unroll
-      for (int k = 0; k < 10; ++k) image_quantities(warm[k], ring1[k]);
+        for (int k = 0; k < 10; ++k) image_quantities(warm[k], ring[k]);
+      }
+      for (int t = 0;;) {
+        if (t >= nb) break;
+        stage1_batch<kLoss, T, 0>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        if (++t >= nb) break;
+        stage1_batch<kLoss, T, 1>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        if (++t >= nb) break;
+        stage1_batch<kLoss, T, 2>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        ++t;
+      }
+      // last tick: stage 2 finishes the segment's last batch
+      __syncthreads();
+      __syncthreads();
+      gb += nb;
     }
+  } else {
+    // stage 2
+    const int col = threadIdx.x - kWaves * kWave;
+    const int wave = wave_id - kWaves;
+    const float dl = *p.dloss;
+    FSeg s;
+    while (next_segment<T>(p, w, s, col)) {
+      const int nb = segment_batches(s);
+      float ring[kRing][kQ];
 #pragma unroll
-    for (int k = 0; k < kRing; ++k)
+      for (int k = 0; k < kRing; ++k)
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) ring2[k][q] = 0.0f;
-
-    for (int t = 0;;) {
-      if (t >= nb) break;
-      fbatch<kLoss, kVec, kNt, T, 0>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
-      buf ^= 1;
-      if (++t >= nb) break;
-      fbatch<kLoss, kVec, kNt, T, 1>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
-      buf ^= 1;
-      if (++t >= nb) break;
-      fbatch<kLoss, kVec, kNt, T, 2>(p, s, tile, ring1, ring2, pre, t, buf, dl, acc);
-      buf ^= 1;
-      ++t;
+        for (int q = 0; q < kQ; ++q) ring[k][q] = 0.0f;
+      // first tick: stage 1 forms the segment's first batch
+      __syncthreads();
+      __syncthreads();
+      for (int t = 0;;) {
+        if (t >= nb) break;
+        stage2_batch<kVec, kNt, T, 0>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        if (++t >= nb) break;
+        stage2_batch<kVec, kNt, T, 1>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        if (++t >= nb) break;
+        stage2_batch<kVec, kNt, T, 2>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        ++t;
+      }
+      gb += nb;
     }
   }
-  if constexpr (kLoss) finish_loss(p, acc, red, is_last);
+  if constexpr (kLoss) finish_loss<kFWaves>(p, acc, red, is_last);
 }
 
 }  // namespace ssim_dev

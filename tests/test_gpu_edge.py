@@ -161,17 +161,18 @@ def test_deterministic_run_to_run():
         np.testing.assert_array_equal(r[k][2], r[0][2])
 
 
-def test_autograd_functions():
+@pytest.mark.parametrize("recompute", [True, False])
+def test_autograd_functions(recompute):
     import torch
 
     import ssim_loss_amd as S
 
-    say("[api] autograd")
+    say(f"[api] autograd recompute={recompute}")
     x, y = make_pair((2, 3, 64, 96), "uniform", 0.1, seed=14)
     dev = torch.device("cuda")
     t1 = torch.from_numpy(x).to(dev).requires_grad_(True)
     t2 = torch.from_numpy(y).to(dev)
-    loss = S.ssim_loss(t1, t2, "valid")
+    loss = S.ssim_loss(t1, t2, "valid", recompute=recompute)
     (0.5 * loss).backward()
     ol, o1, _ = oracle.ssim_loss(x, y, "valid", dloss=0.5)
     check_loss(float(loss.item()), ol)
