@@ -10,7 +10,9 @@ What each function follows is stated in ``ssim_oracle.c``; in short:
   - padding "valid" / "same" with zero fill ("Fully Fused Differentiable SSIM",
     Usage);
   - loss = 1 - mean SSIM; gradients by the chain rule through the adjoint of
-    the blur ("TriSSIM", How it works / Usage).
+    the blur ("TriSSIM", How it works / Usage);
+  - volumes (NCDHW): the same on the 11x11x11 window ("Fully Fused
+    Differentiable SSIM", 3D data).
 """
 from __future__ import annotations
 
@@ -51,6 +53,15 @@ def _load():
     lib.oracle_sample_ssim_f32.argtypes = [vp, vp, i64, i64, i32, i64, i64]
     lib.oracle_sample_ssim_f32.restype = dbl
     lib.oracle_sample_grad_f32.argtypes = [vp, vp, i64, i64, i32, dbl, dbl, i64, i64, vp, vp]
+    lib.oracle_out_shape3.argtypes = [i64, i64, i64, i32, vp, vp, vp]
+    lib.oracle_out_shape3.restype = i32
+    lib.oracle_blur3.argtypes = [vp, i64, i64, i64, i32, vp]
+    lib.oracle_ssim3_volume.argtypes = [vp, vp, i64, i64, i64, i32, dbl, dbl, vp, vp]
+    lib.oracle_ssim3_volume.restype = dbl
+    lib.oracle_ssim3_f32.argtypes = [vp, vp, i64, i64, i64, i64, i64, i32, dbl, vp, vp, vp]
+    lib.oracle_ssim3_f32.restype = i32
+    lib.oracle_sample_grad3_f32.argtypes = [vp, vp, i64, i64, i64, i32, dbl, dbl, i64, i64, i64,
+                                            vp, vp]
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
     _lib = lib
@@ -169,4 +180,74 @@ def sample_grad(x_plane: np.ndarray, y_plane: np.ndarray, padding, M: float, dlo
     _load().oracle_sample_grad_f32(_ptr(x_plane), _ptr(y_plane), H, W, _pad(padding),
                                    float(M), float(dloss), u, v, ctypes.byref(gx),
                                    ctypes.byref(gy))
+    return float(gx.value), float(gy.value)
+
+
+# --------------------------------------------------------------------------- volumes
+
+
+def out_shape3(D: int, H: int, W: int, padding) -> tuple[int, int, int]:
+    do, ho, wo = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _load().oracle_out_shape3(D, H, W, _pad(padding), ctypes.byref(do), ctypes.byref(ho),
+                              ctypes.byref(wo))
+    return int(do.value), int(ho.value), int(wo.value)
+
+
+def blur3(vol: np.ndarray, padding) -> np.ndarray:
+    """B3 (the 11x11x11 window) applied to one D x H x W fp64 volume."""
+    vol = np.ascontiguousarray(vol, np.float64)
+    D, H, W = vol.shape
+    shape = out_shape3(D, H, W, padding)
+    out = np.zeros(tuple(max(n, 0) for n in shape), np.float64)
+    _load().oracle_blur3(_ptr(vol), D, H, W, _pad(padding), _ptr(out))
+    return out
+
+
+def ssim3_loss(x: np.ndarray, y: np.ndarray, padding="same", dloss: float = 1.0,
+               grads: bool = True):
+    """loss = 1 - mean SSIM over an NCDHW batch of volumes, and
+    dloss * d loss / d(x, y).  fp32 inputs are consumed as they are; fp64
+    inputs are used as given.  Returns (loss, grad_x, grad_y) (fp64 gradients,
+    or None when grads is False)."""
+    import math
+
+    assert x.shape == y.shape and x.ndim == 5
+    N, C, D, H, W = x.shape
+    lib = _load()
+    gx = np.zeros(x.shape, np.float64) if grads else None
+    gy = np.zeros(x.shape, np.float64) if grads else None
+    if x.dtype == np.float32 and y.dtype == np.float32:
+        x = np.ascontiguousarray(x)
+        y = np.ascontiguousarray(y)
+        loss = ctypes.c_double()
+        rc = lib.oracle_ssim3_f32(_ptr(x), _ptr(y), N, C, D, H, W, _pad(padding), float(dloss),
+                                  ctypes.byref(loss), _ptr(gx) if grads else None,
+                                  _ptr(gy) if grads else None)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the input (code {rc})")
+        return float(loss.value), gx, gy
+    x = np.ascontiguousarray(x, np.float64)
+    y = np.ascontiguousarray(y, np.float64)
+    Do, Ho, Wo = out_shape3(D, H, W, padding)
+    if min(Do, Ho, Wo) <= 0:
+        raise ValueError("empty SSIM map")
+    M = float(N * C * Do * Ho * Wo)
+    sums = []
+    for n in range(N):
+        for c in range(C):
+            sums.append(lib.oracle_ssim3_volume(
+                _ptr(x[n, c]), _ptr(y[n, c]), D, H, W, _pad(padding), M, float(dloss),
+                _ptr(gx[n, c]) if grads else None, _ptr(gy[n, c]) if grads else None))
+    return 1.0 - math.fsum(sums) / M, gx, gy
+
+
+def sample_grad3(x_vol: np.ndarray, y_vol: np.ndarray, padding, M: float, dloss: float,
+                 t: int, u: int, v: int) -> tuple[float, float]:
+    """(grad_x, grad_y) at voxel (t, u, v) of one fp32 volume pair, for a loss
+    whose mean covers M map entries in total, times dloss."""
+    assert x_vol.dtype == np.float32 and x_vol.flags.c_contiguous
+    D, H, W = x_vol.shape
+    gx, gy = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_sample_grad3_f32(_ptr(x_vol), _ptr(y_vol), D, H, W, _pad(padding), float(M),
+                                    float(dloss), t, u, v, ctypes.byref(gx), ctypes.byref(gy))
     return float(gx.value), float(gy.value)

@@ -451,6 +451,258 @@ void oracle_sample_grad_f32(const float* x, const float* y, int64_t H, int64_t W
 }
 
 /* ---------------------------------------------------------------------- */
+/* Volumes ("Fully Fused Differentiable SSIM", 3D data)                    */
+/* ---------------------------------------------------------------------- */
+
+/* The 3-D SSIM of the page's 3D section keeps the 2-D computation on each XY
+ * slice and adds a Z-axis pass of the same window.  Reading: the window is
+ * the outer product g g g of the same 11 taps (separable, so 2-D blur of each
+ * slice followed by the Z blur is this window exactly); the same constants;
+ * the map is over Do x Ho x Wo output voxels with the same valid/same rule on
+ * every axis; the loss is 1 - the mean over all N*C*Do*Ho*Wo map entries;
+ * gradients go to both volumes.  Volumes are NCDHW. */
+
+static void window3d(double w[WIN][WIN][WIN]) {
+  double g[WIN];
+  oracle_taps(g);
+  for (int a = 0; a < WIN; ++a)
+    for (int b = 0; b < WIN; ++b)
+      for (int c = 0; c < WIN; ++c) w[a][b][c] = g[a] * g[b] * g[c];
+}
+
+int oracle_out_shape3(int64_t D, int64_t H, int64_t W, int padding, int64_t* Do, int64_t* Ho,
+                      int64_t* Wo) {
+  if (padding == PAD_VALID) {
+    *Do = D - (WIN - 1);
+    *Ho = H - (WIN - 1);
+    *Wo = W - (WIN - 1);
+  } else {
+    *Do = D;
+    *Ho = H;
+    *Wo = W;
+  }
+  return (*Do > 0 && *Ho > 0 && *Wo > 0);
+}
+
+/* Voxel with zero fill outside the volume. */
+static double vox(const double* v, int64_t D, int64_t H, int64_t W, int64_t z, int64_t r,
+                  int64_t c) {
+  if (z < 0 || z >= D || r < 0 || r >= H || c < 0 || c >= W) return 0.0;
+  return v[(z * H + r) * W + c];
+}
+
+/* out = B3(in): direct 1331-term windowed sum at every output voxel. */
+void oracle_blur3(const double* in, int64_t D, int64_t H, int64_t W, int padding, double* out) {
+  static double w[WIN][WIN][WIN];
+  window3d(w);
+  int64_t Do, Ho, Wo;
+  if (!oracle_out_shape3(D, H, W, padding, &Do, &Ho, &Wo)) return;
+  const int off = offset_of(padding);
+#pragma omp parallel for schedule(static) collapse(2)
+  for (int64_t k = 0; k < Do; ++k)
+    for (int64_t i = 0; i < Ho; ++i)
+      for (int64_t j = 0; j < Wo; ++j) {
+        double s = 0.0;
+        for (int a = 0; a < WIN; ++a)
+          for (int b = 0; b < WIN; ++b)
+            for (int c = 0; c < WIN; ++c)
+              s += w[a][b][c] * vox(in, D, H, W, k + a - off, i + b - off, j + c - off);
+        out[(k * Ho + i) * Wo + j] = s;
+      }
+}
+
+/* The five windowed sums at output voxel (k, i, j) and the SSIM, exactly as
+ * stats_at in 2-D with the 1331-term window. */
+static stats_t stats_at3(const double* x, const double* y, int64_t D, int64_t H, int64_t W,
+                         int off, const double w[WIN][WIN][WIN], int64_t k, int64_t i, int64_t j) {
+  stats_t s;
+  double mux = 0, muy = 0, sxx = 0, syy = 0, sxy = 0;
+  for (int a = 0; a < WIN; ++a)
+    for (int b = 0; b < WIN; ++b)
+      for (int c = 0; c < WIN; ++c) {
+        double xv = vox(x, D, H, W, k + a - off, i + b - off, j + c - off);
+        double yv = vox(y, D, H, W, k + a - off, i + b - off, j + c - off);
+        double wv = w[a][b][c];
+        mux += wv * xv;
+        muy += wv * yv;
+        sxx += wv * xv * xv;
+        syy += wv * yv * yv;
+        sxy += wv * xv * yv;
+      }
+  const double C1 = oracle_c1(), C2 = oracle_c2();
+  double vx = sxx - mux * mux;
+  double vy = syy - muy * muy;
+  double cxy = sxy - mux * muy;
+  s.mux = mux;
+  s.muy = muy;
+  s.sxx = sxx;
+  s.syy = syy;
+  s.sxy = sxy;
+  s.A1 = 2.0 * mux * muy + C1;
+  s.A2 = 2.0 * cxy + C2;
+  s.B1 = mux * mux + muy * muy + C1;
+  s.B2 = vx + vy + C2;
+  s.S = (s.A1 * s.A2) / (s.B1 * s.B2);
+  return s;
+}
+
+/* Sum of the SSIM map of one volume and, when grad_x or grad_y is non-NULL,
+ * dloss * d(1 - sum/M)/d(voxel), by the same chain rule and gather as the
+ * 2-D plane (the adjoint of B3 gathers over the <= 1331 outputs whose window
+ * covers the voxel). */
+double oracle_ssim3_volume(const double* x, const double* y, int64_t D, int64_t H, int64_t W,
+                           int padding, double M, double dloss, double* grad_x, double* grad_y) {
+  static double w[WIN][WIN][WIN];
+  window3d(w);
+  int64_t Do, Ho, Wo;
+  if (!oracle_out_shape3(D, H, W, padding, &Do, &Ho, &Wo)) return 0.0;
+  const int off = offset_of(padding);
+  const int want_grad = (grad_x != NULL || grad_y != NULL);
+  const int64_t nout = Do * Ho * Wo;
+
+  double* g[5] = {0, 0, 0, 0, 0};
+  if (want_grad)
+    for (int q = 0; q < 5; ++q) g[q] = (double*)malloc(sizeof(double) * (size_t)nout);
+  double* rowsum = (double*)malloc(sizeof(double) * (size_t)(Do * Ho));
+
+#pragma omp parallel for schedule(static) collapse(2)
+  for (int64_t k = 0; k < Do; ++k)
+    for (int64_t i = 0; i < Ho; ++i) {
+      ksum_t acc = {0.0, 0.0};
+      for (int64_t j = 0; j < Wo; ++j) {
+        stats_t s = stats_at3(x, y, D, H, W, off, w, k, i, j);
+        kadd(&acc, s.S);
+        if (want_grad) {
+          double d[5];
+          partials(&s, d);
+          for (int q = 0; q < 5; ++q) g[q][(k * Ho + i) * Wo + j] = -(dloss / M) * d[q];
+        }
+      }
+      rowsum[k * Ho + i] = kval(&acc);
+    }
+  ksum_t tot = {0.0, 0.0};
+  for (int64_t r = 0; r < Do * Ho; ++r) kadd(&tot, rowsum[r]);
+  free(rowsum);
+
+  if (want_grad) {
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t t = 0; t < D; ++t)
+      for (int64_t u = 0; u < H; ++u)
+        for (int64_t v = 0; v < W; ++v) {
+          double gx = 0.0, gy = 0.0;
+          const int64_t q0 = (t * H + u) * W + v;
+          const double xu = x[q0], yu = y[q0];
+          for (int a = 0; a < WIN; ++a) {
+            int64_t k = t - a + off;
+            if (k < 0 || k >= Do) continue;
+            for (int b = 0; b < WIN; ++b) {
+              int64_t i = u - b + off;
+              if (i < 0 || i >= Ho) continue;
+              for (int c = 0; c < WIN; ++c) {
+                int64_t j = v - c + off;
+                if (j < 0 || j >= Wo) continue;
+                int64_t p = (k * Ho + i) * Wo + j;
+                double wv = w[a][b][c];
+                gx += wv * (g[0][p] + 2.0 * xu * g[2][p] + yu * g[4][p]);
+                gy += wv * (g[1][p] + 2.0 * yu * g[3][p] + xu * g[4][p]);
+              }
+            }
+          }
+          if (grad_x) grad_x[q0] = gx;
+          if (grad_y) grad_y[q0] = gy;
+        }
+    for (int q = 0; q < 5; ++q) free(g[q]);
+  }
+  return kval(&tot);
+}
+
+/* loss = 1 - (1/M) sum of the SSIM maps of the N*C volumes (fp32 NCDHW,
+ * widened to fp64 one volume at a time), M = N*C*Do*Ho*Wo; gradients (fp64
+ * NCDHW, nullable) times dloss.  Returns 0, -1 on an empty map, -2 on bad
+ * padding. */
+int oracle_ssim3_f32(const float* x, const float* y, int64_t N, int64_t C, int64_t D, int64_t H,
+                     int64_t W, int padding, double dloss, double* loss, double* grad_x,
+                     double* grad_y) {
+  if (padding != PAD_VALID && padding != PAD_SAME) return -2;
+  int64_t Do, Ho, Wo;
+  if (!oracle_out_shape3(D, H, W, padding, &Do, &Ho, &Wo)) return -1;
+  const double M = (double)N * (double)C * (double)Do * (double)Ho * (double)Wo;
+  const int64_t vol = D * H * W;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)vol);
+  double* yd = (double*)malloc(sizeof(double) * (size_t)vol);
+  ksum_t tot = {0.0, 0.0};
+  for (int64_t pc = 0; pc < N * C; ++pc) {
+    widen(x + pc * vol, xd, vol);
+    widen(y + pc * vol, yd, vol);
+    double s = oracle_ssim3_volume(xd, yd, D, H, W, padding, M, dloss,
+                                   grad_x ? grad_x + pc * vol : NULL,
+                                   grad_y ? grad_y + pc * vol : NULL);
+    kadd(&tot, s);
+  }
+  free(xd);
+  free(yd);
+  *loss = 1.0 - kval(&tot) / M;
+  return 0;
+}
+
+/* Gradient entries at voxel (t, u, v) of one fp32 volume, for a loss whose
+ * mean runs over M map entries in total, times dloss: the same gather, each
+ * needed map value computed on the spot. */
+void oracle_sample_grad3_f32(const float* x, const float* y, int64_t D, int64_t H, int64_t W,
+                             int padding, double M, double dloss, int64_t t, int64_t u, int64_t v,
+                             double* gx, double* gy) {
+  static double w[WIN][WIN][WIN];
+  window3d(w);
+  int64_t Do, Ho, Wo;
+  *gx = 0.0;
+  *gy = 0.0;
+  if (!oracle_out_shape3(D, H, W, padding, &Do, &Ho, &Wo)) return;
+  const int off = offset_of(padding);
+  const int64_t q0 = (t * H + u) * W + v;
+  const double xu = (double)x[q0], yu = (double)y[q0];
+  /* Every map voxel whose window covers (t, u, v) reads volume voxels within
+   * 10 of it on each axis: copy that 21^3 neighbourhood, zero-filled outside
+   * the volume, widened to fp64.  Patch origin: (t, u, v) - 10. */
+  enum { P = 2 * WIN - 1 };
+  double* px = (double*)malloc(sizeof(double) * P * P * P);
+  double* py = (double*)malloc(sizeof(double) * P * P * P);
+  const int64_t z0 = t - (WIN - 1), r0 = u - (WIN - 1), c0 = v - (WIN - 1);
+  for (int a = 0; a < P; ++a)
+    for (int b = 0; b < P; ++b)
+      for (int c = 0; c < P; ++c) {
+        const int64_t zz = z0 + a, rr = r0 + b, cc = c0 + c;
+        const int in = (zz >= 0 && zz < D && rr >= 0 && rr < H && cc >= 0 && cc < W);
+        px[(a * P + b) * P + c] = in ? (double)x[(zz * H + rr) * W + cc] : 0.0;
+        py[(a * P + b) * P + c] = in ? (double)y[(zz * H + rr) * W + cc] : 0.0;
+      }
+  double sx = 0.0, sy = 0.0;
+  for (int a = 0; a < WIN; ++a) {
+    int64_t k = t - a + off;
+    if (k < 0 || k >= Do) continue;
+    for (int b = 0; b < WIN; ++b) {
+      int64_t i = u - b + off;
+      if (i < 0 || i >= Ho) continue;
+      for (int c = 0; c < WIN; ++c) {
+        int64_t j = v - c + off;
+        if (j < 0 || j >= Wo) continue;
+        /* map voxel (k, i, j) reads volume voxels (k + aa - off, ...), which
+         * is patch voxel (k - off - z0 + aa, ...) */
+        stats_t s = stats_at3(px, py, P, P, P, 0, w, k - off - z0, i - off - r0, j - off - c0);
+        double d[5];
+        partials(&s, d);
+        double kk = -(dloss / M) * w[a][b][c];
+        sx += kk * (d[0] + 2.0 * xu * d[2] + yu * d[4]);
+        sy += kk * (d[1] + 2.0 * yu * d[3] + xu * d[4]);
+      }
+    }
+  }
+  free(px);
+  free(py);
+  *gx = sx;
+  *gy = sy;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Threads                                                                 */
 /* ---------------------------------------------------------------------- */
 
