@@ -139,6 +139,102 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch):
     }
 
 
+def volume_algorithmic(shape, padding, eb):
+    """Compulsory HBM bytes and fp32 operations per launch of the volume
+    kernels (forward saves the four loss partials, 16 B per map voxel;
+    backward reads them, reads both volumes and writes both gradients).
+    Operations as for the images, with three 21-operation passes per blurred
+    quantity instead of two."""
+    N, C, D, H, W = shape
+    sh = 10 if padding == "valid" else 0
+    e_in = N * C * D * H * W
+    e_out = N * C * (D - sh) * (H - sh) * (W - sh)
+    blur = 4 * 3 * 21
+    by = {"ssim3d_forward": 2 * eb * e_in + 16 * e_out,
+          "ssim3d_backward": 16 * e_out + 4 * eb * e_in}
+    fl = {"ssim3d_forward": 5 * e_in + (blur + 17 + 5 + 25) * e_out,
+          "ssim3d_backward": blur * e_in + 13 * e_in}
+    return by, fl
+
+
+def bench_volume(args, w, x, y):
+    """Volumes: one step = ssim3d_forward (training: loss + saved partials)
+    then ssim3d_backward (both gradients).  Mvox/s = N*D*H*W per step."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    N, C, D, H, W = x.shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdtype = getattr(torch, args.dtype)
+    eb = torch.empty((), dtype=tdtype).element_size()
+    t1 = torch.from_numpy(x).to(dev).to(tdtype).contiguous()
+    t2 = torch.from_numpy(y).to(dev).to(tdtype).contiguous()
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    maps = S.alloc_saved_maps3d(t1, w.padding)
+    ws = S.workspace_for(dev)
+    dloss = torch.tensor(0.8, dtype=torch.float32, device=dev)
+    g1 = torch.empty_like(t1)
+    g2 = torch.empty_like(t2)
+    fwd = lambda: S.ssim3d_forward(t1, t2, w.padding, loss, maps, ws)
+    bwd = lambda: S.ssim3d_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+    for _ in range(args.warmup):
+        fwd(); bwd()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        fwd(); bwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mvox = N * D * H * W / 1e6
+
+    def per_launch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    kern = {"ssim3d_forward": per_launch_ms(fwd), "ssim3d_backward": per_launch_ms(bwd),
+            "ssim3d_forward(inference)":
+                per_launch_ms(lambda: S.ssim3d_forward(t1, t2, w.padding, loss, None, ws))}
+    by, fl = volume_algorithmic(x.shape, w.padding, eb)
+    dom = max(("ssim3d_forward", "ssim3d_backward"), key=lambda k: kern[k])
+    gbs = by[dom] / (kern[dom] * 1e-3) / 1e9
+    tfs = fl[dom] / (kern[dom] * 1e-3) / 1e12
+    out = {
+        "metric": "Mvox/s fused 3-D SSIM fwd+bwd (volumes)",
+        "value": round(mvox * K / elapsed, 1),
+        "unit": "Mvox/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "float16": "f16 I/O, f32 math",
+                  "bfloat16": "bf16 I/O, f32 math"}[args.dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "shape": list(x.shape), "padding": w.padding,
+                   "design": "saved partials"},
+        "roofline": {"kernel": dom,
+                     "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": by[dom]},
+                     "alu": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
+                             "algorithmic_flops": fl[dom]}},
+        "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+        "loss": float(loss.item()),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 DESIGNS = {
     # design: the launches of one step
     "saved": ("ssim_forward", "ssim_backward"),
@@ -162,6 +258,8 @@ def main():
 
     w = WORKLOADS[args.workload]
     x, y = make_workload(args.workload)
+    if x.ndim == 5:
+        return bench_volume(args, w, x, y)
     N, C, H, W = x.shape
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

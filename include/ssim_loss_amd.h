@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 3
+#define SSIM_ABI_VERSION 4
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -193,6 +193,41 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
 int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
                        int64_t H, int64_t W, int padding, const float* dloss, float* loss,
                        void* workspace, void* grad_img1, void* grad_img2, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Volumes ("Fully Fused Differentiable SSIM", 3D data): NCDHW volumes, the
+ * 11x11x11 window g g g (the same taps on every axis), the same constants,
+ * SSIM formula and loss; valid padding shrinks every axis by 10, same keeps
+ * it (zero fill).  Each volume (and its map) holds at most 2^27 elements;
+ * N*C is unbounded.  Images and gradients are of `dtype`; arithmetic fp32.
+ * Every argument check happens before any HIP call, with the 2-D codes.
+ */
+
+/* Map extent of a D x H x W volume.  Host-only. */
+int ssim3d_map_shape(int64_t D, int64_t H, int64_t W, int padding, int64_t* Do, int64_t* Ho,
+                     int64_t* Wo);
+
+/* Bytes of the saved-maps buffer of a training-mode ssim3d_forward: the four
+ * loss partials (fp32) at every map voxel, 16 * N*C * Do*Ho*Wo bytes, layout
+ * [N*C][4][Do][Ho][Wo]; 16-byte aligned.  0 for invalid arguments. */
+size_t ssim3d_saved_maps_bytes(int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                               int padding);
+
+/* Forward: loss = 1 - mean SSIM over the N*C*Do*Ho*Wo map voxels, one fp32 to
+ * `loss` (device).  saved_maps: NULL (inference) or a device buffer of
+ * ssim3d_saved_maps_bytes(...) bytes that receives the loss partials for
+ * ssim3d_backward.  workspace: as for ssim_forward.  Deterministic. */
+int ssim3d_forward(const void* img1, const void* img2, int dtype, int64_t N, int64_t C, int64_t D,
+                   int64_t H, int64_t W, int padding, float* loss, float* saved_maps,
+                   void* workspace, void* stream);
+
+/* Backward: grad_img1/2 = dloss * d loss / d img1/2 (device outputs of
+ * `dtype`, either may be NULL) from the partials a training-mode
+ * ssim3d_forward saved, by the adjoint of the 3-D blur and the chain rule
+ * ("TriSSIM", How it works, on the 3-D window). */
+int ssim3d_backward(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
+                    int64_t C, int64_t D, int64_t H, int64_t W, int padding,
+                    const float* saved_maps, void* grad_img1, void* grad_img2, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,10 @@ Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
 One-pass step, for an upstream gradient known in advance:
   loss_and_grad(img1, img2, padding="valid", weight=1.0)
       -> (weight-free loss, weight * dloss/dimg1, weight * dloss/dimg2)
+Volumes (NCDHW, "Fully Fused Differentiable SSIM", 3D data):
+  ssim3d_forward, ssim3d_backward, ssim3d_saved_maps_bytes, ssim3d_map_shape
+  ssim3d_loss(vol1, vol2, padding="same", train=True) -> 1 - mean SSIM
+  fused_ssim3d(vol1, vol2, padding="same", train=True) -> mean SSIM
 """
 from __future__ import annotations
 
@@ -85,6 +89,15 @@ def lib() -> ctypes.CDLL:
         L.ssim_backward_recompute.restype = i32
         L.ssim_backward_recompute.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp,
                                               vp]
+        L.ssim3d_map_shape.restype = i32
+        L.ssim3d_map_shape.argtypes = [i64, i64, i64, i32, vp, vp, vp]
+        L.ssim3d_saved_maps_bytes.restype = sz
+        L.ssim3d_saved_maps_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        L.ssim3d_forward.restype = i32
+        L.ssim3d_forward.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp]
+        L.ssim3d_backward.restype = i32
+        L.ssim3d_backward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, vp, vp, vp,
+                                      vp]
         L.ssim_loss_and_grad.restype = i32
         L.ssim_loss_and_grad.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                          vp]
@@ -146,7 +159,7 @@ def _dtype_code(t) -> int:
     return SSIM_DTYPE[str(t.dtype).replace("torch.", "")]
 
 
-def _check_image(t, name):
+def _check_image(t, name, ndim=4):
     import torch
 
     if not isinstance(t, torch.Tensor):
@@ -155,10 +168,11 @@ def _check_image(t, name):
         raise TypeError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
     if t.device.type != "cuda":
         raise TypeError(f"{name} must be a GPU tensor, got device {t.device}")
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be NCHW (4-D), got shape {tuple(t.shape)}")
+    layout = "NCHW" if ndim == 4 else "NCDHW"
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {layout} ({ndim}-D), got shape {tuple(t.shape)}")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous NCHW")
+        raise ValueError(f"{name} must be contiguous {layout}")
 
 
 def ssim_forward(img1, img2, padding, loss, saved_maps, workspace) -> None:
@@ -206,9 +220,9 @@ def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) 
         raise SsimError(rc, "ssim_backward")
 
 
-def _check_pair_and_grads(img1, img2, grads):
-    _check_image(img1, "img1")
-    _check_image(img2, "img2")
+def _check_pair_and_grads(img1, img2, grads, ndim=4):
+    _check_image(img1, "img1", ndim)
+    _check_image(img2, "img2", ndim)
     if img1.shape != img2.shape:
         raise ValueError("img1 and img2 must have the same shape")
     if img1.dtype != img2.dtype:
@@ -362,3 +376,105 @@ def loss_and_grad(img1, img2, padding: str = "valid", weight=1.0, grad1: bool = 
     g2 = torch.empty_like(img2) if grad2 else None
     ssim_loss_and_grad(img1.detach(), img2.detach(), padding, dl, loss, workspace_for(dev), g1, g2)
     return loss, g1, g2
+
+
+# --------------------------------------------------------------------------- volumes
+
+
+def ssim3d_map_shape(D: int, H: int, W: int, padding) -> tuple[int, int, int]:
+    do, ho, wo = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().ssim3d_map_shape(int(D), int(H), int(W), _pad(padding), ctypes.byref(do),
+                                ctypes.byref(ho), ctypes.byref(wo))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim3d_map_shape")
+    return int(do.value), int(ho.value), int(wo.value)
+
+
+def ssim3d_saved_maps_bytes(N: int, C: int, D: int, H: int, W: int, padding) -> int:
+    return int(lib().ssim3d_saved_maps_bytes(int(N), int(C), int(D), int(H), int(W),
+                                             _pad(padding)))
+
+
+def ssim3d_forward(vol1, vol2, padding, loss, saved_maps, workspace) -> None:
+    """Calls the C ``ssim3d_forward`` on torch's current stream (saved_maps
+    may be None: inference)."""
+    _check_pair_and_grads(vol1, vol2, (), ndim=5)
+    N, C, D, H, W = vol1.shape
+    rc = lib().ssim3d_forward(_dptr(vol1), _dptr(vol2), _dtype_code(vol1), N, C, D, H, W,
+                              _pad(padding), _dptr(loss), _dptr(saved_maps), _dptr(workspace),
+                              _stream_ptr(vol1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim3d_forward")
+
+
+def ssim3d_backward(dloss, vol1, vol2, padding, saved_maps, grad_vol1, grad_vol2) -> None:
+    """Calls the C ``ssim3d_backward`` on torch's current stream."""
+    _check_pair_and_grads(vol1, vol2, (grad_vol1, grad_vol2), ndim=5)
+    N, C, D, H, W = vol1.shape
+    rc = lib().ssim3d_backward(_dptr(dloss), _dptr(vol1), _dptr(vol2), _dtype_code(vol1), N, C,
+                               D, H, W, _pad(padding), _dptr(saved_maps), _dptr(grad_vol1),
+                               _dptr(grad_vol2), _stream_ptr(vol1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim3d_backward")
+
+
+def alloc_saved_maps3d(vol1, padding) -> "torch.Tensor":
+    import torch
+
+    N, C, D, H, W = vol1.shape
+    nbytes = ssim3d_saved_maps_bytes(N, C, D, H, W, padding)
+    if nbytes == 0:
+        raise SsimError(-2, "ssim3d_saved_maps_bytes")
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=vol1.device)
+
+
+def _make_function3d():
+    import torch
+
+    class _Ssim3dLoss(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, vol1, vol2, padding, train):
+            vol1 = vol1.detach()
+            vol2 = vol2.detach()
+            loss = torch.empty((), dtype=torch.float32, device=vol1.device)
+            maps = alloc_saved_maps3d(vol1, padding) if train else None
+            ssim3d_forward(vol1, vol2, padding, loss, maps, workspace_for(vol1.device))
+            ctx.padding = padding
+            ctx.train = train
+            if train:
+                ctx.save_for_backward(vol1, vol2, maps)
+            return loss
+
+        @staticmethod
+        def backward(ctx, dloss):
+            if not ctx.train:
+                raise RuntimeError("ssim3d_loss was called with train=False; no gradient saved")
+            vol1, vol2, maps = ctx.saved_tensors
+            want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+            g1 = torch.empty_like(vol1) if want1 else None
+            g2 = torch.empty_like(vol2) if want2 else None
+            dl = dloss.detach().to(dtype=torch.float32).contiguous()
+            ssim3d_backward(dl, vol1, vol2, ctx.padding, maps, g1, g2)
+            return g1, g2, None, None
+
+    return _Ssim3dLoss
+
+
+_fn3d = None
+
+
+def ssim3d_loss(vol1, vol2, padding: str = "same", train: bool = True):
+    """loss = 1 - mean SSIM of two NCDHW volumes (the 11x11x11 window), with
+    gradients for whichever of vol1 / vol2 requires them."""
+    global _fn3d
+    if _fn3d is None:
+        _fn3d = _make_function3d()
+    _check_pair_and_grads(vol1, vol2, (), ndim=5)
+    _pad(padding)
+    return _fn3d.apply(vol1, vol2, padding, bool(train))
+
+
+def fused_ssim3d(vol1, vol2, padding: str = "same", train: bool = True):
+    """Mean SSIM of two volumes ("Fully Fused Differentiable SSIM", 3D data:
+    fused_ssim3d on [BS, CH, D, H, W])."""
+    return 1.0 - ssim3d_loss(vol1, vol2, padding, train)

@@ -343,6 +343,150 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Volumes (NCDHW)
+
+struct Shape3 {
+  int64_t N, C, D, H, W, Do, Ho, Wo, vols;
+  size_t img_bytes, map_bytes;
+};
+
+int check_shape3(int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int padding, int dtype,
+                 Shape3* s) {
+  if (padding != SSIM_PAD_VALID && padding != SSIM_PAD_SAME) return SSIM_ERR_PADDING;
+  if (dtype != SSIM_DTYPE_F32 && dtype != SSIM_DTYPE_F16 && dtype != SSIM_DTYPE_BF16)
+    return SSIM_ERR_DTYPE;
+  if (N <= 0 || C <= 0 || D <= 0 || H <= 0 || W <= 0) return SSIM_ERR_SHAPE;
+  const int64_t sh = padding == SSIM_PAD_VALID ? 10 : 0;
+  const int64_t Do = D - sh, Ho = H - sh, Wo = W - sh;
+  if (Do <= 0 || Ho <= 0 || Wo <= 0) return SSIM_ERR_SHAPE;
+  // one volume (and its map) holds at most 2^27 elements, so that every
+  // byte offset inside it fits 32 bits with room for the out-of-range marker
+  const int64_t lim = (int64_t)1 << 27;
+  if (W > lim || H > lim / W || D > lim / (H * W)) return SSIM_ERR_OVERFLOW;
+  if (N > (int64_t)1 << 40 || C > ((int64_t)1 << 40) / N) return SSIM_ERR_OVERFLOW;
+  const int64_t vols = N * C;
+  if (vols > ((int64_t)1 << 58) / (D * H * W)) return SSIM_ERR_OVERFLOW;
+  s->N = N; s->C = C; s->D = D; s->H = H; s->W = W; s->Do = Do; s->Ho = Ho; s->Wo = Wo;
+  s->vols = vols;
+  s->img_bytes = (size_t)(vols * D * H * W) * elem_bytes(dtype);
+  s->map_bytes = (size_t)(vols * Do * Ho * Wo) * 4 * sizeof(float);
+  return SSIM_OK;
+}
+
+// One resident wave of workgroups over (tile-column, output slice) work: a
+// depth range of at least kVMinSlices slices of one tile-column each, or
+// whole tile-columns.
+int launch_vol(const DeviceInfo* d, int dtype, int which, VolParams& p, void* stream) {
+  p.tiles_x = (p.out_w + kVT - 1) / kVT;
+  p.tiles_y = (p.out_h + kVT - 1) / kVT;
+  p.cols = p.cols * p.tiles_x * p.tiles_y;  // volumes * tiles
+  int64_t resident = (int64_t)d->cus * d->occ[dtype][which];
+  if (resident > kMaxBlocks) resident = kMaxBlocks;
+  int64_t G;
+  if (p.cols >= resident) {
+    p.parts = 1;
+    p.per_block = (int)((p.cols + resident - 1) / resident);
+    G = (p.cols + p.per_block - 1) / p.per_block;
+  } else {
+    int64_t parts = resident / p.cols;
+    const int64_t max_parts = (p.out_d + kVMinSlices - 1) / kVMinSlices;
+    if (parts > max_parts) parts = max_parts;
+    if (parts < 1) parts = 1;
+    p.parts = (int)parts;
+    p.per_block = 1;
+    G = p.cols * parts;
+  }
+  void* args[] = {&p};
+  if (hipLaunchKernel(kernel_table(dtype)[which], dim3((unsigned)G), dim3(kind_threads(which)), args,
+                      0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSIM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
+}
+
+void fill_vol(VolParams& p, const Shape3& s, int padding) {
+  p.D = (int)s.D; p.H = (int)s.H; p.W = (int)s.W;
+  p.Do = (int)s.Do; p.Ho = (int)s.Ho; p.Wo = (int)s.Wo;
+  p.vol = s.D * s.H * s.W;
+  p.map_vol = s.Do * s.Ho * s.Wo;
+  p.cols = s.vols;
+  const double M = (double)s.vols * (double)p.map_vol;
+  p.k_m2 = (float)(-2.0 / M);
+  p.inv_m = 1.0 / M;
+  (void)padding;
+}
+
+int vol_forward_impl(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
+                     int64_t D, int64_t H, int64_t W, int padding, float* loss, float* saved_maps,
+                     void* workspace, void* stream) {
+  if (!img1 || !img2 || !loss || !workspace) return SSIM_ERR_NULL;
+  Shape3 s;
+  int rc = check_shape3(N, C, D, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if (misaligned(img1, dtype) || misaligned(img2, dtype)) return SSIM_ERR_SHAPE;
+  if (saved_maps && ((uintptr_t)saved_maps & 15u)) return SSIM_ERR_SHAPE;
+  const void* outs[3] = {loss, saved_maps, workspace};
+  const size_t outb[3] = {sizeof(float), saved_maps ? s.map_bytes : 0, sizeof(Workspace)};
+  for (int k = 0; k < 3; ++k) {
+    if (overlaps(outs[k], outb[k], img1, s.img_bytes) || overlaps(outs[k], outb[k], img2, s.img_bytes))
+      return SSIM_ERR_ALIAS;
+    for (int l = k + 1; l < 3; ++l)
+      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
+  }
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+  VolParams p;
+  memset(&p, 0, sizeof(p));
+  fill_vol(p, s, padding);
+  p.off = padding == SSIM_PAD_VALID ? 0 : 5;
+  p.in_d = (int)s.D; p.in_h = (int)s.H; p.in_w = (int)s.W;
+  p.out_d = (int)s.Do; p.out_h = (int)s.Ho; p.out_w = (int)s.Wo;
+  p.x = img1;
+  p.y = img2;
+  p.maps = saved_maps;
+  p.loss = loss;
+  p.ws = static_cast<Workspace*>(workspace);
+  return launch_vol(d, dtype, saved_maps ? kKVolFwdTrain : kKVolFwdInfer, p, stream);
+}
+
+int vol_backward_impl(const float* dloss, const void* img1, const void* img2, int dtype,
+                      int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int padding,
+                      const float* saved_maps, void* grad_img1, void* grad_img2, void* stream) {
+  if (!dloss || !img1 || !img2 || !saved_maps) return SSIM_ERR_NULL;
+  Shape3 s;
+  int rc = check_shape3(N, C, D, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if ((uintptr_t)saved_maps & 15u) return SSIM_ERR_SHAPE;
+  if (misaligned(img1, dtype) || misaligned(img2, dtype) || misaligned(grad_img1, dtype) ||
+      misaligned(grad_img2, dtype))
+    return SSIM_ERR_SHAPE;
+  const void* ins[4] = {dloss, img1, img2, saved_maps};
+  const size_t inb[4] = {sizeof(float), s.img_bytes, s.img_bytes, s.map_bytes};
+  void* outs[2] = {grad_img1, grad_img2};
+  for (int k = 0; k < 2; ++k)
+    for (int l = 0; l < 4; ++l)
+      if (overlaps(outs[k], s.img_bytes, ins[l], inb[l])) return SSIM_ERR_ALIAS;
+  if (overlaps(grad_img1, s.img_bytes, grad_img2, s.img_bytes)) return SSIM_ERR_ALIAS;
+  if (!grad_img1 && !grad_img2) return SSIM_OK;
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+  VolParams p;
+  memset(&p, 0, sizeof(p));
+  fill_vol(p, s, padding);
+  p.off = padding == SSIM_PAD_VALID ? 10 : 5;
+  p.in_d = (int)s.Do; p.in_h = (int)s.Ho; p.in_w = (int)s.Wo;
+  p.out_d = (int)s.D; p.out_h = (int)s.H; p.out_w = (int)s.W;
+  p.x = img1;
+  p.y = img2;
+  p.maps = const_cast<float*>(saved_maps);
+  p.dloss = dloss;
+  p.gx = grad_img1;
+  p.gy = grad_img2;
+  return launch_vol(d, dtype, kKVolBwd, p, stream);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -429,6 +573,39 @@ int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N,
   if (!loss) return SSIM_ERR_NULL;
   return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
                         grad_img2, stream);
+}
+
+int ssim3d_map_shape(int64_t D, int64_t H, int64_t W, int padding, int64_t* Do, int64_t* Ho,
+                     int64_t* Wo) {
+  if (!Do || !Ho || !Wo) return SSIM_ERR_NULL;
+  Shape3 s;
+  const int rc = check_shape3(1, 1, D, H, W, padding, SSIM_DTYPE_F32, &s);
+  if (rc != SSIM_OK) return rc;
+  *Do = s.Do;
+  *Ho = s.Ho;
+  *Wo = s.Wo;
+  return SSIM_OK;
+}
+
+size_t ssim3d_saved_maps_bytes(int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                               int padding) {
+  Shape3 s;
+  if (check_shape3(N, C, D, H, W, padding, SSIM_DTYPE_F32, &s) != SSIM_OK) return 0;
+  return s.map_bytes;
+}
+
+int ssim3d_forward(const void* img1, const void* img2, int dtype, int64_t N, int64_t C, int64_t D,
+                   int64_t H, int64_t W, int padding, float* loss, float* saved_maps,
+                   void* workspace, void* stream) {
+  return vol_forward_impl(img1, img2, dtype, N, C, D, H, W, padding, loss, saved_maps, workspace,
+                          stream);
+}
+
+int ssim3d_backward(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
+                    int64_t C, int64_t D, int64_t H, int64_t W, int padding,
+                    const float* saved_maps, void* grad_img1, void* grad_img2, void* stream) {
+  return vol_backward_impl(dloss, img1, img2, dtype, N, C, D, H, W, padding, saved_maps,
+                           grad_img1, grad_img2, stream);
 }
 
 }  // extern "C"

@@ -9,6 +9,7 @@
 #pragma once
 
 #include "ssim_fused.hpp"
+#include "ssim_vol.hpp"
 
 namespace ssim_dev {
 // threads per workgroup of each kernel kind: the recomputing kernels run two
@@ -26,9 +27,16 @@ enum KernelKind {
   kKLossGrad,          // loss and both gradients in one pass
   kKLossGradStream,
   kKLossGradUnaligned,
+  kKVolFwdInfer,       // volumes: forward, loss only
+  kKVolFwdTrain,       // volumes: forward, loss + saved partials
+  kKVolBwd,            // volumes: backward from the saved partials
   kKinds
 };
-__host__ __device__ constexpr int kind_threads(int k) { return k >= kKRecomp ? kFThreads : kThreads; }
+__host__ __device__ constexpr int kind_threads(int k) {
+  return (k >= kKRecomp && k <= kKLossGradUnaligned) ? kFThreads : kThreads;
+}
+// the parameter block each kind takes
+__host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdInfer; }
 }  // namespace ssim_dev
 
 #define SSIM_KERNEL_(NAME, BODY)                                                           \
@@ -37,6 +45,15 @@ __host__ __device__ constexpr int kind_threads(int k) { return k >= kKRecomp ? k
   }
 #define SSIM_FKERNEL_(NAME, BODY)                                                          \
   __global__ __launch_bounds__(ssim_dev::kFThreads) void NAME(const ssim_dev::Params p) {  \
+    BODY(p);                                                                               \
+  }
+
+// the volume kernels' working set is a 44-register depth window and a few
+// LDS reads in flight; without an occupancy target the scheduler hoists
+// reads into registers far past that
+#define SSIM_VKERNEL_(NAME, WAVES, BODY)                                                   \
+  __global__ __launch_bounds__(ssim_dev::kThreads) __attribute__((amdgpu_waves_per_eu(WAVES))) \
+  void NAME(const ssim_dev::VolParams p) {                                                 \
     BODY(p);                                                                               \
   }
 
@@ -63,6 +80,11 @@ __host__ __device__ constexpr int kind_threads(int k) { return k >= kKRecomp ? k
                (ssim_dev::fused_body<true, true, true, T>))                                 \
   SSIM_FKERNEL_(ssim_loss_grad_unaligned##NAME##kernel,                                     \
                (ssim_dev::fused_body<true, false, false, T>))                              \
+  SSIM_VKERNEL_(ssim3d_fwd_infer##NAME##kernel, 4,                                         \
+                (ssim_dev::vol_body<ssim_dev::kFwdInfer, false, T>))                        \
+  SSIM_VKERNEL_(ssim3d_fwd_train##NAME##kernel, 3,                                         \
+                (ssim_dev::vol_body<ssim_dev::kFwdTrain, false, T>))                        \
+  SSIM_VKERNEL_(ssim3d_bwd##NAME##kernel, 3, (ssim_dev::vol_body<ssim_dev::kBwd, false, T>)) \
   }                                                                                        \
   const void* const* TABLE() {                                                             \
     static const void* const t[ssim_dev::kKinds] = {                                      \
@@ -77,7 +99,10 @@ __host__ __device__ constexpr int kind_threads(int k) { return k >= kKRecomp ? k
         (const void*)ssim_bwd_recompute_unaligned##NAME##kernel,                           \
         (const void*)ssim_loss_grad##NAME##kernel,                                         \
         (const void*)ssim_loss_grad_stream##NAME##kernel,                                  \
-        (const void*)ssim_loss_grad_unaligned##NAME##kernel};                              \
+        (const void*)ssim_loss_grad_unaligned##NAME##kernel,                               \
+        (const void*)ssim3d_fwd_infer##NAME##kernel,                                       \
+        (const void*)ssim3d_fwd_train##NAME##kernel,                                       \
+        (const void*)ssim3d_bwd##NAME##kernel};                                            \
     return t;                                                                              \
   }
 

@@ -9,6 +9,9 @@ arrays.
 
 The workloads stand in for render-vs-ground-truth frames of a Gaussian
 splatting train step (the pages measure "1080p" frames and name no dataset).
+The volume workload has the shape of the 3-D usage example of "Fully Fused
+Differentiable SSIM" (3D data): 2 x 3 x 96^3, uniform voxels; the second
+volume is a noisy copy of the first, as for the images.
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    shape: tuple[int, int, int, int]  # N, C, H, W
+    shape: tuple[int, ...]            # N, C, H, W (images) or N, C, D, H, W (volumes)
     padding: str                      # "valid" | "same"
     kind: str                         # "uniform" | "field"
     noise: float                      # std of the Gaussian noise added to img1 to form img2
@@ -29,8 +32,9 @@ class Workload:
 
     @property
     def pixels(self) -> int:
-        n, _, h, w = self.shape
-        return n * h * w
+        """N*H*W for images, N*D*H*W (voxels) for volumes."""
+        n = self.shape[0]
+        return n * int(np.prod(self.shape[2:]))
 
 
 WORKLOADS = {
@@ -41,6 +45,7 @@ WORKLOADS = {
         Workload("1080p-valid", (1, 3, 1080, 1920), "valid", "field", 0.03, 0),
         Workload("1080p-same", (1, 3, 1080, 1920), "same", "field", 0.03, 0),
         Workload("4k-batch8", (8, 3, 2160, 3840), "valid", "uniform", 0.05, 0, True),
+        Workload("vol-96", (2, 3, 96, 96, 96), "same", "uniform", 0.05, 0),
     ]
 }
 
@@ -92,7 +97,18 @@ def _one_image(rng: np.random.Generator, C: int, H: int, W: int, kind: str,
 
 def make_pair(shape, kind: str = "uniform", noise: float = 0.05, seed: int = 0,
               per_image_seed: bool = False) -> tuple[np.ndarray, np.ndarray]:
-    """img1, img2 as contiguous fp32 NCHW arrays."""
+    """img1, img2 as contiguous fp32 NCHW arrays (or NCDHW volumes, for which
+    only the "uniform" and "constant" kinds exist)."""
+    if len(shape) == 5:
+        rng = np.random.default_rng(seed)
+        if kind == "uniform":
+            a = rng.random(shape)
+        elif kind == "constant":
+            a = np.broadcast_to(rng.random((shape[0], shape[1], 1, 1, 1)), shape).copy()
+        else:
+            raise ValueError(f"volumes have no kind {kind!r}")
+        b = np.clip(a + rng.normal(0.0, noise, a.shape), 0.0, 1.0) if noise > 0 else a.copy()
+        return np.ascontiguousarray(a.astype(np.float32)), np.ascontiguousarray(b.astype(np.float32))
     N, C, H, W = shape
     if not per_image_seed:
         rng = np.random.default_rng(seed)

@@ -18,13 +18,14 @@ HEADER = os.path.join(ROOT, "include", "ssim_loss_amd.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssim_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssim(?:3d)?_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["ssim_forward", "ssim_backward", "ssim_forward_typed", "ssim_backward_typed",
-              "ssim_backward_recompute", "ssim_loss_and_grad",
+              "ssim_backward_recompute", "ssim_loss_and_grad", "ssim3d_forward",
+              "ssim3d_backward", "ssim3d_saved_maps_bytes", "ssim3d_map_shape",
               "ssim_saved_maps_bytes", "ssim_workspace_bytes", "ssim_strerror",
               "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
         assert n in names
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert S.ssim_abi_version() == 3
+    assert S.ssim_abi_version() == 4
     for code in range(0, -9, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
@@ -173,6 +174,35 @@ def test_loss_and_grad_argument_errors_return_before_any_hip_call():
     assert _lag(lib, loss=0x100000 + 16) == -5      # loss inside img2
     assert _lag(lib, ws=0x900000 + 4096) == -5      # workspace overlaps a gradient
     assert _lag(lib, loss=0x300000 + 8) == -5       # loss inside the workspace
+
+
+def test_volume_shapes_and_argument_errors():
+    lib = S.lib()
+    assert S.ssim3d_map_shape(96, 96, 96, "same") == (96, 96, 96)
+    assert S.ssim3d_map_shape(12, 20, 11, "valid") == (2, 10, 1)
+    assert S.ssim3d_saved_maps_bytes(2, 3, 96, 96, 96, "same") == 16 * 6 * 96 ** 3
+    assert S.ssim3d_saved_maps_bytes(1, 1, 10, 20, 20, "valid") == 0
+    fwd = lambda **kw: lib.ssim3d_forward(
+        kw.get("x", 0x10000), kw.get("y", 0x200000), kw.get("dt", 0), 1, 1, kw.get("D", 16), 16,
+        16, kw.get("pad", 1), kw.get("loss", 0x400000), kw.get("maps", None), kw.get("ws", 0x500000),
+        None)
+    assert fwd(x=None) == -1
+    assert fwd(loss=None) == -1
+    assert fwd(pad=4) == -3
+    assert fwd(dt=7) == -8
+    assert fwd(D=0) == -2
+    assert fwd(D=5, pad=0) == -2
+    assert fwd(x=0x10002) == -2
+    assert fwd(maps=0x600008) == -2
+    assert fwd(loss=0x10000 + 64) == -5
+    assert fwd(D=1 << 20) == -4       # a volume of more than 2^27 voxels
+    bwd = lambda **kw: lib.ssim3d_backward(
+        0x1000, 0x10000, 0x200000, 0, 1, 1, 16, 16, 16, 1, kw.get("maps", 0x600000),
+        kw.get("g1", 0x800000), kw.get("g2", 0x900000), None)
+    assert bwd(maps=None) == -1
+    assert bwd(g1=0x600000 + 16) == -5
+    assert bwd(g1=0x900000 + 4) == -5
+    assert bwd(g1=None, g2=None) == 0
 
 
 def test_python_binding_rejects_cpu_tensors():
