@@ -47,10 +47,13 @@ def parse():
     ap.add_argument("--workload", default="1080p-valid")
     ap.add_argument("--dtype", default="float32", choices=["float32", "float16", "bfloat16"],
                     help="storage type of images and gradients (arithmetic is fp32)")
-    ap.add_argument("--design", default="one-pass", choices=["saved", "recompute", "one-pass"],
+    ap.add_argument("--design", default="one-pass",
+                    choices=["saved", "recompute", "one-pass", "one-pass-ref"],
                     help="saved: forward saves the statistics, backward reads them; "
                          "recompute: loss-only forward, backward recomputes the statistics; "
-                         "one-pass: loss and gradients in one launch")
+                         "one-pass: loss and gradients in one launch; "
+                         "one-pass-ref: the same with the reference's statistics cached and "
+                         "only the first image's gradient")
     ap.add_argument("--all-kernels", action="store_true",
                     help="also time the kernels of the other designs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -76,7 +79,9 @@ def algorithmic_bytes(shape, padding, eb=4):
     input element) and writes four fp32 maps (16 B per map entry); backward
     reads the maps (16 B per entry), x and y (2 eb per element) and writes
     both gradients (2 eb per element).  The recomputing kernels read x, y and
-    write both gradients (4 eb per element); the inference forward reads x, y."""
+    write both gradients (4 eb per element); the inference forward reads x, y.
+    With a cached reference: x, y and the cached map (4 B per map entry) in,
+    grad_x out."""
     N, C, H, W = shape
     Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
     e_in = N * C * H * W
@@ -85,7 +90,8 @@ def algorithmic_bytes(shape, padding, eb=4):
             "ssim_backward": 16 * e_out + 4 * eb * e_in,
             "ssim_forward(inference)": 2 * eb * e_in,
             "ssim_backward_recompute": 4 * eb * e_in,
-            "ssim_loss_and_grad": 4 * eb * e_in}
+            "ssim_loss_and_grad": 4 * eb * e_in,
+            "ssim_loss_and_grad_ref": 3 * eb * e_in + 4 * e_out}
 
 
 def algorithmic_flops(shape, padding):
@@ -105,9 +111,11 @@ def algorithmic_flops(shape, padding):
     fwd = 5 * e_in + (blur + 17 + 5) * e_out
     bwd_from_stats = (17 + 25) * e_out + (blur + 13) * e_in
     recompute = 5 * e_in + (blur + 17 + 25) * e_out + (blur + 13) * e_in
+    blur3 = 3 * 2 * 21  # three quantities
+    ref_step = 5 * e_in + (blur3 + 17 + 5 + 25) * e_out + (blur3 + 7) * e_in
     return {"ssim_forward": fwd, "ssim_forward(inference)": fwd,
             "ssim_backward": bwd_from_stats, "ssim_backward_recompute": recompute,
-            "ssim_loss_and_grad": recompute + 5 * e_out}
+            "ssim_loss_and_grad": recompute + 5 * e_out, "ssim_loss_and_grad_ref": ref_step}
 
 
 def cpu_baseline(x, y, padding, pixels_per_image_batch):
@@ -240,6 +248,9 @@ DESIGNS = {
     "saved": ("ssim_forward", "ssim_backward"),
     "recompute": ("ssim_forward(inference)", "ssim_backward_recompute"),
     "one-pass": ("ssim_loss_and_grad",),
+    # a fixed reference with its statistics cached (computed once, outside
+    # the step), only the first image's gradient
+    "one-pass-ref": ("ssim_loss_and_grad_ref",),
 }
 
 
@@ -273,6 +284,8 @@ def main():
     dloss = torch.tensor(0.8, dtype=torch.float32, device=dev)  # as under a weighted loss
     g1 = torch.empty_like(t1)
     g2 = torch.empty_like(t2)
+    ref = (S.reference_stats(t2, w.padding)
+           if args.design == "one-pass-ref" or args.all_kernels else None)
     torch.cuda.synchronize()
 
     launches = {
@@ -283,6 +296,8 @@ def main():
             lambda: S.ssim_backward_recompute(dloss, t1, t2, w.padding, g1, g2),
         "ssim_loss_and_grad":
             lambda: S.ssim_loss_and_grad(t1, t2, w.padding, dloss, loss, ws, g1, g2),
+        "ssim_loss_and_grad_ref":
+            lambda: S.ssim_loss_and_grad_ref(t1, t2, ref, w.padding, dloss, loss, ws, g1),
     }
     step_launches = [launches[k] for k in DESIGNS[args.design]]
 
@@ -321,6 +336,7 @@ def main():
         return e0.elapsed_time(e1) / K
 
     timed = [k for k in launches if (maps is not None or k not in ("ssim_forward", "ssim_backward"))
+             and (ref is not None or k != "ssim_loss_and_grad_ref")
              and (args.all_kernels or k in DESIGNS[args.design])]
     kern = {k: per_launch_ms(launches[k]) for k in timed}
 

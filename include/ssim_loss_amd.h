@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 4
+#define SSIM_ABI_VERSION 5
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -193,6 +193,38 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
 int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
                        int64_t H, int64_t W, int padding, const float* dloss, float* loss,
                        void* workspace, void* grad_img1, void* grad_img2, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Cached reference statistics.  In a training run the second image is often
+ * a fixed reference (the ground-truth view, with only the first image
+ * differentiable: "Fully Fused Differentiable SSIM", Constraints).  Of the
+ * statistics the kernels blur, B(y - 1/2) depends on the reference alone; it
+ * can be computed once per reference and reused by every step that compares
+ * against it.  (The pages' SSIMULACRA2 port caches reference-side work the
+ * same way; here it is the one reference-only statistic of the SSIM basis.)
+ */
+
+/* Bytes of the cached statistics of an N x C x H x W reference: one fp32
+ * plane per image plane over the map, row pitch Wo rounded up to 4, i.e.
+ * 4 * N*C * Ho * roundup(Wo, 4) bytes; 16-byte aligned.  0 for invalid
+ * arguments.  Host-only. */
+size_t ssim_reference_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding);
+
+/* Writes B(img2 - 1/2) (the reference's blurred mean, shifted) to `ref`
+ * (device, ssim_reference_bytes(...) bytes).  img2: device image of
+ * `dtype`.  The result is valid for that exact image, shape and padding. */
+int ssim_reference_stats(const void* img2, int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
+                         int padding, float* ref, void* stream);
+
+/* As ssim_loss_and_grad with grad_img2 = NULL, reading B(img2 - 1/2) from
+ * `ref` (ssim_reference_stats of this img2) instead of forming it: loss =
+ * 1 - mean SSIM and grad_img1 = *dloss * d loss / d img1 in one launch, one
+ * blur fewer in each direction.  img2 is still read (the other statistics mix
+ * both images).  grad_img1 may be NULL (loss only). */
+int ssim_loss_and_grad_ref(const void* img1, const void* img2, const float* ref, int dtype,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                           const float* dloss, float* loss, void* workspace, void* grad_img1,
+                           void* stream);
 
 /* ---------------------------------------------------------------------------
  * Volumes ("Fully Fused Differentiable SSIM", 3D data): NCDHW volumes, the

@@ -24,6 +24,11 @@ Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
 One-pass step, for an upstream gradient known in advance:
   loss_and_grad(img1, img2, padding="valid", weight=1.0)
       -> (weight-free loss, weight * dloss/dimg1, weight * dloss/dimg2)
+Cached reference statistics (a fixed second image, only the first one
+differentiable):
+  ref = reference_stats(img2, padding="valid")
+  loss_and_grad_ref(img1, img2, ref, padding="valid", weight=1.0)
+      -> (loss, weight * dloss/dimg1)
 Volumes (NCDHW, "Fully Fused Differentiable SSIM", 3D data):
   ssim3d_forward, ssim3d_backward, ssim3d_saved_maps_bytes, ssim3d_map_shape
   ssim3d_loss(vol1, vol2, padding="same", train=True) -> 1 - mean SSIM
@@ -98,6 +103,13 @@ def lib() -> ctypes.CDLL:
         L.ssim3d_backward.restype = i32
         L.ssim3d_backward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, vp, vp, vp,
                                       vp]
+        L.ssim_reference_bytes.restype = sz
+        L.ssim_reference_bytes.argtypes = [i64, i64, i64, i64, i32]
+        L.ssim_reference_stats.restype = i32
+        L.ssim_reference_stats.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
+        L.ssim_loss_and_grad_ref.restype = i32
+        L.ssim_loss_and_grad_ref.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp,
+                                             vp, vp, vp]
         L.ssim_loss_and_grad.restype = i32
         L.ssim_loss_and_grad.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                          vp]
@@ -376,6 +388,66 @@ def loss_and_grad(img1, img2, padding: str = "valid", weight=1.0, grad1: bool = 
     g2 = torch.empty_like(img2) if grad2 else None
     ssim_loss_and_grad(img1.detach(), img2.detach(), padding, dl, loss, workspace_for(dev), g1, g2)
     return loss, g1, g2
+
+
+# --------------------------------------------------------------------------- cached reference
+
+
+def ssim_reference_bytes(N: int, C: int, H: int, W: int, padding) -> int:
+    return int(lib().ssim_reference_bytes(int(N), int(C), int(H), int(W), _pad(padding)))
+
+
+def ssim_reference_stats(img2, padding, ref) -> None:
+    """Calls the C ``ssim_reference_stats`` on torch's current stream."""
+    _check_image(img2, "img2")
+    N, C, H, W = img2.shape
+    rc = lib().ssim_reference_stats(_dptr(img2), _dtype_code(img2), N, C, H, W, _pad(padding),
+                                    _dptr(ref), _stream_ptr(img2))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_reference_stats")
+
+
+def ssim_loss_and_grad_ref(img1, img2, ref, padding, dloss, loss, workspace, grad_img1) -> None:
+    """Calls the C ``ssim_loss_and_grad_ref`` on torch's current stream."""
+    _check_pair_and_grads(img1, img2, (grad_img1,))
+    N, C, H, W = img1.shape
+    rc = lib().ssim_loss_and_grad_ref(_dptr(img1), _dptr(img2), _dptr(ref), _dtype_code(img1), N,
+                                      C, H, W, _pad(padding), _dptr(dloss), _dptr(loss),
+                                      _dptr(workspace), _dptr(grad_img1), _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_loss_and_grad_ref")
+
+
+def reference_stats(img2, padding: str = "valid") -> "torch.Tensor":
+    """The cached statistics of a fixed reference image (a device fp32 tensor
+    of ssim_reference_bytes bytes), for loss_and_grad_ref."""
+    import torch
+
+    N, C, H, W = img2.shape
+    nbytes = ssim_reference_bytes(N, C, H, W, padding)
+    if nbytes == 0:
+        raise SsimError(-2, "ssim_reference_bytes")
+    ref = torch.empty(nbytes // 4, dtype=torch.float32, device=img2.device)
+    ssim_reference_stats(img2.detach(), padding, ref)
+    return ref
+
+
+def loss_and_grad_ref(img1, img2, ref, padding: str = "valid", weight=1.0, grad1: bool = True):
+    """(loss, weight * d loss / d img1) in one launch, with the reference's
+    statistics read from `ref` (reference_stats of this img2)."""
+    import torch
+
+    _check_pair_and_grads(img1, img2, ())
+    dev = img1.device
+    if isinstance(weight, torch.Tensor):
+        dl = weight.detach().to(device=dev, dtype=torch.float32).reshape(()).contiguous()
+    else:
+        dl = torch.tensor(float(weight), dtype=torch.float32, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    g1 = torch.empty_like(img1) if grad1 else None
+    ssim_loss_and_grad_ref(img1.detach(), img2.detach(), ref, padding, dl, loss,
+                           workspace_for(dev), g1)
+    return loss, g1
 
 
 # --------------------------------------------------------------------------- volumes

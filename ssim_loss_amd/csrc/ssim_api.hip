@@ -267,9 +267,11 @@ int backward_impl(const float* dloss, const void* img1, const void* img2, int dt
 // each workgroup gets at least kRecompMinRows rows.
 constexpr int kRecompMinRows = 40;
 
+// ref (optional, with loss): the cached statistics of img2 written by
+// ssim_reference_stats; then only grad_img1 is formed.
 int recompute_impl(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
                    int64_t C, int64_t H, int64_t W, int padding, float* loss, void* workspace,
-                   void* grad_img1, void* grad_img2, void* stream) {
+                   void* grad_img1, void* grad_img2, void* stream, const float* ref = nullptr) {
   if (!dloss || !img1 || !img2) return SSIM_ERR_NULL;
   if (loss && !workspace) return SSIM_ERR_NULL;
   Shape s;
@@ -278,13 +280,15 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   if (misaligned(img1, dtype) || misaligned(img2, dtype) || misaligned(grad_img1, dtype) ||
       misaligned(grad_img2, dtype))
     return SSIM_ERR_SHAPE;
-  const void* ins[3] = {dloss, img1, img2};
-  const size_t inb[3] = {sizeof(float), s.img_bytes, s.img_bytes};
+  if (ref && ((uintptr_t)ref & 15u)) return SSIM_ERR_SHAPE;
+  const size_t ref_bytes = ref ? s.map_bytes / 4 : 0;  // one fp32 plane of the map layout
+  const void* ins[4] = {dloss, img1, img2, ref};
+  const size_t inb[4] = {sizeof(float), s.img_bytes, s.img_bytes, ref_bytes};
   const void* outs[4] = {grad_img1, grad_img2, loss, workspace};
   const size_t outb[4] = {s.img_bytes, s.img_bytes, sizeof(float),
                           loss ? sizeof(Workspace) : 0};
   for (int k = 0; k < 4; ++k) {
-    for (int l = 0; l < 3; ++l)
+    for (int l = 0; l < 4; ++l)
       if (overlaps(outs[k], outb[k], ins[l], inb[l])) return SSIM_ERR_ALIAS;
     for (int l = k + 1; l < 4; ++l)
       if (overlaps(outs[k], outb[k], outs[l], outb[l])) return SSIM_ERR_ALIAS;
@@ -326,8 +330,14 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   const bool vec = (s.W % 4 == 0) && ((uintptr_t)img1 % al == 0) && ((uintptr_t)img2 % al == 0) &&
                    ((uintptr_t)grad_img1 % al == 0) && ((uintptr_t)grad_img2 % al == 0);
   const bool stream_st = 4 * s.img_bytes > kStreamBytes;
-  const int which = loss ? (!vec ? kKLossGradUnaligned : stream_st ? kKLossGradStream : kKLossGrad)
-                         : (!vec ? kKRecompUnaligned : stream_st ? kKRecompStream : kKRecomp);
+  int which = loss ? (!vec ? kKLossGradUnaligned : stream_st ? kKLossGradStream : kKLossGrad)
+                   : (!vec ? kKRecompUnaligned : stream_st ? kKRecompStream : kKRecomp);
+  if (ref) {
+    which = !vec ? kKLossGradRefUnaligned : stream_st ? kKLossGradRefStream : kKLossGradRef;
+    p.maps = const_cast<float*>(ref);
+    p.map_pitch = (int)s.pitch;
+    p.map_plane = s.Ho * s.pitch;
+  }
   // one resident wave of workgroups, each with an equal run of (strip-column,
   // row) pairs, and at least kRecompMinRows rows each
   const int64_t rows = p.cols * (int64_t)p.out_h;
@@ -487,6 +497,33 @@ int vol_backward_impl(const float* dloss, const void* img1, const void* img2, in
   return launch_vol(d, dtype, kKVolBwd, p, stream);
 }
 
+// The cached reference statistics of img2: B(img2 - 1/2) on the map, one
+// fp32 plane per image plane with the saved-maps row pitch.
+int ref_stats_impl(const void* img2, int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
+                   int padding, float* ref, void* stream) {
+  if (!img2 || !ref) return SSIM_ERR_NULL;
+  Shape s;
+  int rc = check_shape(N, C, H, W, padding, dtype, &s);
+  if (rc != SSIM_OK) return rc;
+  if (misaligned(img2, dtype) || ((uintptr_t)ref & 15u)) return SSIM_ERR_SHAPE;
+  if (overlaps(ref, s.map_bytes / 4, img2, s.img_bytes)) return SSIM_ERR_ALIAS;
+  const DeviceInfo* d = nullptr;
+  rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+  Params p;
+  memset(&p, 0, sizeof(p));
+  const int off = padding == SSIM_PAD_VALID ? 0 : 5;
+  fill_geometry(p, (int)s.H, (int)s.W, (int)s.W, s.H * s.W, (int)s.Ho, (int)s.Wo, off, s.planes);
+  p.x = img2;
+  p.y = img2;
+  p.img_plane = s.H * s.W;
+  p.img_w = (int)s.W;
+  p.maps = ref;
+  p.map_pitch = (int)s.pitch;
+  p.map_plane = s.Ho * s.pitch;
+  return launch(d, dtype, kKRefStats, p, stream);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -573,6 +610,26 @@ int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N,
   if (!loss) return SSIM_ERR_NULL;
   return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
                         grad_img2, stream);
+}
+
+size_t ssim_reference_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding) {
+  Shape s;
+  if (check_shape(N, C, H, W, padding, SSIM_DTYPE_F32, &s) != SSIM_OK) return 0;
+  return s.map_bytes / 4;
+}
+
+int ssim_reference_stats(const void* img2, int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
+                         int padding, float* ref, void* stream) {
+  return ref_stats_impl(img2, dtype, N, C, H, W, padding, ref, stream);
+}
+
+int ssim_loss_and_grad_ref(const void* img1, const void* img2, const float* ref, int dtype,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int padding,
+                           const float* dloss, float* loss, void* workspace, void* grad_img1,
+                           void* stream) {
+  if (!loss || !ref) return SSIM_ERR_NULL;
+  return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
+                        nullptr, stream, ref);
 }
 
 int ssim3d_map_shape(int64_t D, int64_t H, int64_t W, int padding, int64_t* Do, int64_t* Ho,

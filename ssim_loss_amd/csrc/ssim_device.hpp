@@ -134,7 +134,9 @@ struct Workspace {
   double partial[kMaxBlocks];
 };
 
-enum Mode { kFwdInfer = 0, kFwdTrain = 1, kBwd = 2 };
+// kRef: blur a reference image alone and store its blurred mean B(y - 1/2)
+// (the statistic that depends on the reference only), for reuse across steps
+enum Mode { kFwdInfer = 0, kFwdTrain = 1, kBwd = 2, kRef = 3 };
 
 // Storage type of images and gradients (the arithmetic is fp32 throughout;
 // maps are always fp32).
@@ -445,7 +447,12 @@ template <int MODE, bool kVec, bool kNt, int T>
 __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
                                         const Group<MODE, kVec>& g, const float (&o)[kQ][4],
                                         float dl, double& acc) {
-  if constexpr (MODE != kBwd) {
+  if constexpr (MODE == kRef) {
+    // the reference's blurred mean, 16 contiguous bytes of its map row
+    (void)dl;
+    (void)acc;
+    st4<kNt>(s.out[0], g.base, make_float4(o[1][0], o[1][1], o[1][2], o[1][3]));
+  } else if constexpr (MODE != kBwd) {
     float s4 = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -681,6 +688,8 @@ __device__ __forceinline__ void strip_body(const Params& p) {
         const float* mp = p.maps + plane * 4 * p.map_plane;
 #pragma unroll
         for (int k = 0; k < 4; ++k) s.out[k] = make_rsrc(mp + k * p.map_plane, p.map_plane * 4);
+      } else if constexpr (MODE == kRef) {
+        s.out[0] = make_rsrc(p.maps + plane * p.map_plane, p.map_plane * 4);
       }
       s.out_row = (unsigned)p.map_pitch * 4u;
       s.out_elem = 4u;
@@ -711,7 +720,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     }
   }
 
-  if constexpr (MODE != kBwd) finish_loss<kWaves>(p, acc, red, is_last);
+  if constexpr (MODE == kFwdInfer || MODE == kFwdTrain) finish_loss<kWaves>(p, acc, red, is_last);
 }
 
 }  // namespace ssim_dev

@@ -27,13 +27,17 @@ enum KernelKind {
   kKLossGrad,          // loss and both gradients in one pass
   kKLossGradStream,
   kKLossGradUnaligned,
+  kKLossGradRef,       // loss and grad_x in one pass, with cached reference statistics
+  kKLossGradRefStream,
+  kKLossGradRefUnaligned,
+  kKRefStats,          // the cached reference statistics of an image
   kKVolFwdInfer,       // volumes: forward, loss only
   kKVolFwdTrain,       // volumes: forward, loss + saved partials
   kKVolBwd,            // volumes: backward from the saved partials
   kKinds
 };
 __host__ __device__ constexpr int kind_threads(int k) {
-  return (k >= kKRecomp && k <= kKLossGradUnaligned) ? kFThreads : kThreads;
+  return (k >= kKRecomp && k <= kKLossGradRefUnaligned) ? kFThreads : kThreads;
 }
 // the parameter block each kind takes
 __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdInfer; }
@@ -43,8 +47,10 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
   __global__ __launch_bounds__(ssim_dev::kThreads) void NAME(const ssim_dev::Params p) {   \
     BODY(p);                                                                               \
   }
+// 8-wave workgroups: two per CU need at most 128 VGPRs (4 waves per SIMD)
 #define SSIM_FKERNEL_(NAME, BODY)                                                          \
-  __global__ __launch_bounds__(ssim_dev::kFThreads) void NAME(const ssim_dev::Params p) {  \
+  __global__ __launch_bounds__(ssim_dev::kFThreads) __attribute__((amdgpu_waves_per_eu(4))) \
+  void NAME(const ssim_dev::Params p) {                                                    \
     BODY(p);                                                                               \
   }
 
@@ -80,6 +86,14 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
                (ssim_dev::fused_body<true, true, true, T>))                                 \
   SSIM_FKERNEL_(ssim_loss_grad_unaligned##NAME##kernel,                                     \
                (ssim_dev::fused_body<true, false, false, T>))                              \
+  SSIM_FKERNEL_(ssim_loss_grad_ref##NAME##kernel,                                          \
+                (ssim_dev::fused_body<true, true, false, T, true>))                        \
+  SSIM_FKERNEL_(ssim_loss_grad_ref_stream##NAME##kernel,                                   \
+                (ssim_dev::fused_body<true, true, true, T, true>))                         \
+  SSIM_FKERNEL_(ssim_loss_grad_ref_unaligned##NAME##kernel,                                \
+                (ssim_dev::fused_body<true, false, false, T, true>))                       \
+  SSIM_KERNEL_(ssim_ref_stats##NAME##kernel,                                               \
+               (ssim_dev::strip_body<ssim_dev::kRef, false, false, T>))                    \
   SSIM_VKERNEL_(ssim3d_fwd_infer##NAME##kernel, 4,                                         \
                 (ssim_dev::vol_body<ssim_dev::kFwdInfer, false, T>))                        \
   SSIM_VKERNEL_(ssim3d_fwd_train##NAME##kernel, 3,                                         \
@@ -100,6 +114,10 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
         (const void*)ssim_loss_grad##NAME##kernel,                                         \
         (const void*)ssim_loss_grad_stream##NAME##kernel,                                  \
         (const void*)ssim_loss_grad_unaligned##NAME##kernel,                               \
+        (const void*)ssim_loss_grad_ref##NAME##kernel,                                     \
+        (const void*)ssim_loss_grad_ref_stream##NAME##kernel,                              \
+        (const void*)ssim_loss_grad_ref_unaligned##NAME##kernel,                           \
+        (const void*)ssim_ref_stats##NAME##kernel,                                         \
         (const void*)ssim3d_fwd_infer##NAME##kernel,                                       \
         (const void*)ssim3d_fwd_train##NAME##kernel,                                       \
         (const void*)ssim3d_bwd##NAME##kernel};                                            \

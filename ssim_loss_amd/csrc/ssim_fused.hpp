@@ -64,6 +64,8 @@ struct FSeg {
   int i0;               // map row completed by the first batch row: u0 - off2
   int own_r1;           // the loss counts map rows [i0, own_r1) ...
   int own_c1;           // ... and map columns [jm0, own_c1) (clipped to the map)
+  rsrc_t ref;           // cached reference statistics: B(y - 1/2) map plane
+  unsigned ref_row;     // its row pitch, bytes
 };
 
 // This lane's pixel of x and y in image row r (0 outside the image).
@@ -84,22 +86,27 @@ __device__ __forceinline__ void image_quantities(const float (&v)[2], float (&q)
 }
 
 // column pass of one row through a 12-slot ring: the new row goes into slot
-// (base + 10) % 12, and the output is the 11-tap sum over slots base..base+10
-template <int kBase>
+// (base + 10) % 12, and the output is the 11-tap sum over slots base..base+10.
+// Quantity kSkip (if any) is not blurred.
+template <int kBase, int kSkip = -1>
 __device__ __forceinline__ void ring_column(float (&ring)[kRing][kQ], float (&cs)[kQ]) {
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) cs[q] = tap(0) * ring[kBase % kRing][q];
+  for (int q = 0; q < kQ; ++q) cs[q] = q == kSkip ? 0.0f : tap(0) * ring[kBase % kRing][q];
 #pragma unroll
   for (int a = 1; a < 11; ++a)
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) cs[q] = __builtin_fmaf(tap(a), ring[(kBase + a) % kRing][q], cs[q]);
+    for (int q = 0; q < kQ; ++q)
+      if (q != kSkip) cs[q] = __builtin_fmaf(tap(a), ring[(kBase + a) % kRing][q], cs[q]);
 }
 
 // row pass: 4 adjacent outputs of each of the 4 quantities from 16 columns of
-// a tile row starting at column c (16-byte aligned)
+// a tile row starting at column c (16-byte aligned); quantity kSkip (if any)
+// is left alone
+template <int kSkip = -1>
 __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ][4]) {
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
+    if (q == kSkip) continue;
     const float* src = row0 + q * (kRows * kFTileW) + c;
     float v[16];
 #pragma unroll
@@ -123,12 +130,16 @@ __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ
 // Stage 1 of batch t (PH = t mod 3): the column pass of image rows u0 + 4t
 // .. +3 into the tile, then the row pass of tile row `wave` -> SSIM terms,
 // loss and partials, written back over that row.  Two barriers.
-template <bool kLoss, int T, int PH>
+template <bool kLoss, int T, int PH, bool kRef>
 __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              float (&ring)[kRing][kQ], float (&pre)[kRows][2],
                                              int t, int buf, int col, int wave, int lane,
                                              double& acc) {
+  constexpr int kSkip = kRef ? 1 : -1;  // with a cached reference, B(y') is read, not blurred
+  const int i = s.i0 + 4 * t + wave;
+  const bool irow = (unsigned)i < (unsigned)p.map_h;
+  const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
   float cur[kRows][2];
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
@@ -145,25 +156,37 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
     float cs[kQ];
     image_quantities(cur[m], ring[(kB0 + m + 10) % kRing]);
     switch (m) {  // m is a compile-time constant after unrolling
-      case 0: ring_column<kB0 + 0>(ring, cs); break;
-      case 1: ring_column<kB0 + 1>(ring, cs); break;
-      case 2: ring_column<kB0 + 2>(ring, cs); break;
-      default: ring_column<kB0 + 3>(ring, cs); break;
+      case 0: ring_column<kB0 + 0, kSkip>(ring, cs); break;
+      case 1: ring_column<kB0 + 1, kSkip>(ring, cs); break;
+      case 2: ring_column<kB0 + 2, kSkip>(ring, cs); break;
+      default: ring_column<kB0 + 3, kSkip>(ring, cs); break;
     }
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) tile[buf][q][m][col] = cs[q];
+    for (int q = 0; q < kQ; ++q)
+      if (q != kSkip) tile[buf][q][m][col] = cs[q];
   }
   __syncthreads();
 
   // row pass: wave w -> map row i0 + 4t + w; lane l -> map columns
   // jm0 + 4l .. 4l+3.  The partials go back into the row just read.
-  const int i = s.i0 + 4 * t + wave;
-  const bool irow = (unsigned)i < (unsigned)p.map_h;
-  const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
+  float muy_ref[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (kRef) {
+    // the cached B(y - 1/2) at this lane's 4 map entries (0 outside the map)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int jm = s.jm0 + 4 * lr + c;
+      const bool ok = irow && (unsigned)jm < (unsigned)p.map_w;
+      muy_ref[c] = ld1(s.ref, ok ? (unsigned)i * s.ref_row + (unsigned)jm * 4u : kOob);
+    }
+  }
   float part[kQ][4];
   if (irow) {
     float o[kQ][4];
-    row_pass(&tile[buf][0][wave][0], 4 * lr, o);
+    row_pass<kSkip>(&tile[buf][0][wave][0], 4 * lr, o);
+    if constexpr (kRef) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[1][c] = muy_ref[c];
+    }
     const bool own_row = kLoss && i < s.own_r1;
     float s4 = 0.0f;
 #pragma unroll
@@ -191,8 +214,9 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
   if (lane < kFMapLanes) {
 #pragma unroll
     for (int k = 0; k < kQ; ++k)
-      *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
-          make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
+      if (k != kSkip)
+        *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
+            make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
   }
   __syncthreads();
 }
@@ -201,11 +225,14 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
 // left in the tile (lane t owns map column jm0 + t; written back into the
 // same column), then the row pass of tile row `wave` and the chain rule for
 // gradient row u0 + 4t + wave - 10.  Two barriers.
-template <bool kVec, bool kNt, int T, int PH>
+template <bool kVec, bool kNt, int T, int PH, bool kRef>
 __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              float (&ring)[kRing][kQ], int t, int buf, int col,
                                              int wave, int lane, float dl) {
+  // with a cached reference only grad_x is formed: m1 (which feeds grad_y
+  // alone) is neither blurred nor used
+  constexpr int kSkip = kRef ? 1 : -1;
   constexpr unsigned kEb = img_bytes<T>();
   // the gradient row this wave finishes, and its images for the chain rule
   // (loaded first, so their latency hides behind the column pass).  Memory
@@ -235,16 +262,18 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   for (int m = 0; m < kRows; ++m) {
     constexpr int kB0 = 4 * PH;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) ring[(kB0 + m + 10) % kRing][q] = tile[buf][q][m][col];
+    for (int q = 0; q < kQ; ++q)
+      if (q != kSkip) ring[(kB0 + m + 10) % kRing][q] = tile[buf][q][m][col];
     float cs[kQ];
     switch (m) {
-      case 0: ring_column<kB0 + 0>(ring, cs); break;
-      case 1: ring_column<kB0 + 1>(ring, cs); break;
-      case 2: ring_column<kB0 + 2>(ring, cs); break;
-      default: ring_column<kB0 + 3>(ring, cs); break;
+      case 0: ring_column<kB0 + 0, kSkip>(ring, cs); break;
+      case 1: ring_column<kB0 + 1, kSkip>(ring, cs); break;
+      case 2: ring_column<kB0 + 2, kSkip>(ring, cs); break;
+      default: ring_column<kB0 + 3, kSkip>(ring, cs); break;
     }
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) tile[buf][q][m][col] = cs[q];
+    for (int q = 0; q < kQ; ++q)
+      if (q != kSkip) tile[buf][q][m][col] = cs[q];
   }
   __syncthreads();
 
@@ -253,22 +282,23 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   if (grow) {
     const int lr = lane < kFGradLanes ? lane : kFGradLanes - 1;
     float o[kQ][4];
-    row_pass(&tile[buf][0][wave][0], 4 * lr, o);
+    row_pass<kSkip>(&tile[buf][0][wave][0], 4 * lr, o);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float xs = xv[c] - kShift, ys = yv[c] - kShift, d = xv[c] - yv[c];
       g1[c] = dl * __builtin_fmaf(d, o[2][c], __builtin_fmaf(ys, o[3][c], o[0][c]));
-      g2[c] = dl * __builtin_fmaf(-d, o[2][c], __builtin_fmaf(xs, o[3][c], o[1][c]));
+      if constexpr (!kRef)
+        g2[c] = dl * __builtin_fmaf(-d, o[2][c], __builtin_fmaf(xs, o[3][c], o[1][c]));
     }
   }
   if constexpr (kVec) {
     st_img4<T, kNt>(s.out[0], gbase, g1);
-    st_img4<T, kNt>(s.out[1], gbase, g2);
+    if constexpr (!kRef) st_img4<T, kNt>(s.out[1], gbase, g2);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       st_img<T, kNt>(s.out[0], goff[c], g1[c]);
-      st_img<T, kNt>(s.out[1], goff[c], g2[c]);
+      if constexpr (!kRef) st_img<T, kNt>(s.out[1], goff[c], g2[c]);
     }
   }
   __syncthreads();
@@ -329,6 +359,10 @@ __device__ __forceinline__ bool next_segment(const Params& p, FShare& w, FSeg& s
     // range's own share)
     s.own_r1 = (row_end == p.out_h) ? p.map_h : row_end - p.off2;
     s.own_c1 = (strip == p.strips - 1) ? p.map_w : s.jm0 + kFOut;
+    // cached reference statistics (the map buffer with its row pitch), if any
+    s.ref = make_rsrc(p.maps ? p.maps + plane * p.map_plane : p.x,
+                      p.maps ? p.map_plane * 4 : 0);
+    s.ref_row = (unsigned)p.map_pitch * 4u;
     return true;
   }
 }
@@ -347,7 +381,9 @@ __device__ __forceinline__ int segment_batches(const FSeg& s) {
 // batches before it in this workgroup) mod 2; per segment each group passes
 // 2 (nb + 1) barriers (stage 2 idles through the first tick, stage 1
 // through the last), so the two loops meet at every barrier.
-template <bool kLoss, bool kVec, bool kNt, int T>
+// kRef: B(y - 1/2) comes from a cached map (p.maps, the layout the
+// reference-statistics kernel writes) and only grad_x is formed.
+template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false>
 __device__ __forceinline__ void fused_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kFTileW];
   __shared__ double red[kFWaves];
@@ -380,11 +416,14 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       }
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage1_batch<kLoss, T, 0>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+                                          acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 1>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+                                          acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 2>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane, acc);
+        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+                                          acc);
         ++t;
       }
       // last tick: stage 2 finishes the segment's last batch
@@ -410,11 +449,11 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       __syncthreads();
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage2_batch<kVec, kNt, T, 0>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 0, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 1>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 1, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 2>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 2, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
         ++t;
       }
       gb += nb;

@@ -24,7 +24,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["ssim_forward", "ssim_backward", "ssim_forward_typed", "ssim_backward_typed",
-              "ssim_backward_recompute", "ssim_loss_and_grad", "ssim3d_forward",
+              "ssim_backward_recompute", "ssim_loss_and_grad", "ssim_reference_bytes",
+              "ssim_reference_stats", "ssim_loss_and_grad_ref", "ssim3d_forward",
               "ssim3d_backward", "ssim3d_saved_maps_bytes", "ssim3d_map_shape",
               "ssim_saved_maps_bytes", "ssim_workspace_bytes", "ssim_strerror",
               "ssim_abi_version", "ssim_taps", "ssim_map_shape"]:
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert S.ssim_abi_version() == 4
+    assert S.ssim_abi_version() == 5
     for code in range(0, -9, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
@@ -174,6 +175,27 @@ def test_loss_and_grad_argument_errors_return_before_any_hip_call():
     assert _lag(lib, loss=0x100000 + 16) == -5      # loss inside img2
     assert _lag(lib, ws=0x900000 + 4096) == -5      # workspace overlaps a gradient
     assert _lag(lib, loss=0x300000 + 8) == -5       # loss inside the workspace
+
+
+def test_reference_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    assert S.ssim_reference_bytes(1, 3, 1080, 1920, "valid") == 4 * 3 * 1070 * 1912
+    assert S.ssim_reference_bytes(1, 1, 5, 30, "valid") == 0
+    st = lambda **kw: lib.ssim_reference_stats(kw.get("img", 0x10000), kw.get("dt", 0), 1, 1, 64,
+                                               64, kw.get("pad", 0), kw.get("ref", 0x300000), None)
+    assert st(img=None) == -1
+    assert st(ref=None) == -1
+    assert st(dt=4) == -8
+    assert st(pad=2) == -3
+    assert st(ref=0x300004) == -2
+    assert st(ref=0x10000 + 256) == -5
+    lg = lambda **kw: lib.ssim_loss_and_grad_ref(
+        0x10000, 0x100000, kw.get("ref", 0x300000), 0, 1, 1, 64, 64, 0, 0x1000,
+        kw.get("loss", 0x2000), 0x500000, kw.get("g1", 0x900000), None)
+    assert lg(ref=None) == -1
+    assert lg(loss=None) == -1
+    assert lg(ref=0x300008) == -2
+    assert lg(g1=0x300000 + 64) == -5     # gradient overlaps the cached statistics
 
 
 def test_volume_shapes_and_argument_errors():
