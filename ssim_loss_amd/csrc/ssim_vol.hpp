@@ -10,7 +10,7 @@
 //
 // One workgroup (256 lanes) owns a 16 x 16 tile of output (i, j) positions of
 // one volume and marches along depth.  Per depth step it stages the 26 x 26
-// input tile of one slice in LDS, runs the X pass (26 x 16 partial sums) and
+// input tile of one slice in LDS (loaded one step ahead into registers), runs the X pass (26 x 16 partial sums) and
 // the Y pass (16 x 16) through LDS, and each lane shifts its four XY-blurred
 // values into an 11-deep register window whose 11-tap sum is the Z pass (a
 // shift keeps the register indices fixed without unrolling the depth loop,
@@ -84,20 +84,27 @@ struct VolSeg {
   int k0, nk;           // output slices [k0, k0 + nk)
 };
 
-// Stage one input slice's tile (slice index kin, rows i0 - off .., columns
-// j0 - off ..) into LDS as the four quantities to be blurred.  Outside the
-// blurred input's extent the value is that of a zero input: for the forward
-// x = y = 0 (so x' = y' = -1/2), for the backward a zero partial.
+// One slice's input tile, held in registers between its loads and its LDS
+// store: each lane owns up to kVIters positions of the 26 x 26 tile (the
+// last iteration is partial).  Forward: x and y; backward: the 4 partials.
+constexpr int kVIters = (kVIn * kVIn + kThreads - 1) / kThreads;
+template <int MODE>
+struct VolPre {
+  float v[kVIters][MODE == kBwd ? 4 : 2];
+};
+
+// Issue the loads of input slice kin's tile (rows i0 - off .., columns
+// j0 - off ..).  Outside the blurred input's extent a load reads 0 (an
+// out-of-range offset): for the forward x = y = 0, for the backward a zero
+// partial.  Every lane runs every iteration; positions past the tile use an
+// out-of-range offset too.
 template <int MODE, int T>
-__device__ __forceinline__ void vol_stage(const VolParams& p, const VolSeg& s, int kin,
-                                          float (&A)[kQ][kVIn][kVInP]) {
+__device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, int kin,
+                                         VolPre<MODE>& pre) {
   constexpr unsigned kEb = img_bytes<T>();
-  constexpr int kIters = (kVIn * kVIn + kThreads - 1) / kThreads;
   const bool kok = (unsigned)kin < (unsigned)p.in_d;
-  // every lane runs the same iterations (loads of positions past the tile
-  // use an out-of-range offset); only the LDS writes are guarded
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
+  for (int it = 0; it < kVIters; ++it) {
     const int t = threadIdx.x + it * kThreads;
     const bool in_tile = t < kVIn * kVIn;
     const int tt = in_tile ? t : 0;
@@ -108,18 +115,30 @@ __device__ __forceinline__ void vol_stage(const VolParams& p, const VolSeg& s, i
     const unsigned e = ok ? (unsigned)(((int64_t)kin * p.in_h + ii) * p.in_w + jj) : 0u;
     if constexpr (MODE == kBwd) {
       const unsigned off = ok ? e * 4u : kOob;
-      float v[kQ];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) v[q] = ld1(s.in[q], off);
-      if (in_tile) {
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) A[q][r][c] = v[q];
-      }
+      for (int q = 0; q < kQ; ++q) pre.v[it][q] = ld1(s.in[q], off);
     } else {
       const unsigned off = ok ? e * kEb : kOob;
-      const float xv = ld_img<T>(s.in[0], off), yv = ld_img<T>(s.in[1], off);
-      const float xs = xv - kShift, ys = yv - kShift, d = xv - yv;
-      if (in_tile) {
+      pre.v[it][0] = ld_img<T>(s.in[0], off);
+      pre.v[it][1] = ld_img<T>(s.in[1], off);
+    }
+  }
+}
+
+// Store a loaded tile into LDS as the four quantities to be blurred.
+template <int MODE>
+__device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ][kVIn][kVInP]) {
+#pragma unroll
+  for (int it = 0; it < kVIters; ++it) {
+    const int t = threadIdx.x + it * kThreads;
+    if (t < kVIn * kVIn) {
+      const int r = t / kVIn, c = t - r * kVIn;
+      if constexpr (MODE == kBwd) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) A[q][r][c] = pre.v[it][q];
+      } else {
+        const float xv = pre.v[it][0], yv = pre.v[it][1];
+        const float xs = xv - kShift, ys = yv - kShift, d = xv - yv;
         A[0][r][c] = xs;
         A[1][r][c] = ys;
         A[2][r][c] = d * d;
@@ -129,15 +148,18 @@ __device__ __forceinline__ void vol_stage(const VolParams& p, const VolSeg& s, i
   }
 }
 
-// One depth step: stage input slice kin, blur it in X and Y, shift the
-// lane's window down by one slice with the new values in slot 10, and return
-// the Z-pass sum over slots 0 .. 10 in o.
+// One depth step on input slice kin, whose tile `pre` holds: store it to LDS,
+// issue the loads of slice kin + 1 into `pre` (their latency hides behind
+// this step), blur in X and Y, shift the lane's window down by one slice with
+// the new values in slot 10, and return the Z-pass sum over slots 0 .. 10 in
+// o.
 template <int MODE, int T>
 __device__ __forceinline__ void vol_step(const VolParams& p, const VolSeg& s, int kin,
-                                         float (&A)[kQ][kVIn][kVInP],
+                                         VolPre<MODE>& pre, float (&A)[kQ][kVIn][kVInP],
                                          float (&Bx)[kQ][kVIn][kVT], float (&win)[11][kQ],
                                          float (&o)[kQ]) {
-  vol_stage<MODE, T>(p, s, kin, A);
+  vol_store<MODE>(pre, A);
+  vol_load<MODE, T>(p, s, kin + 1, pre);
   __syncthreads();
   // X pass: 26 rows x 16 columns of partial sums
   constexpr int kXIters = (kVIn * kVT + kThreads - 1) / kThreads;
@@ -257,9 +279,11 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       for (int q = 0; q < kQ; ++q) win[k][q] = 0.0f;
     float o[kQ];
     const int kin0 = s.k0 - p.off;
-    for (int k = 0; k < 10; ++k) vol_step<MODE, T>(p, s, kin0 + k, A, Bx, win, o);
+    VolPre<MODE> pre;
+    vol_load<MODE, T>(p, s, kin0, pre);
+    for (int k = 0; k < 10; ++k) vol_step<MODE, T>(p, s, kin0 + k, pre, A, Bx, win, o);
     for (int n = 0; n < s.nk; ++n) {
-      vol_step<MODE, T>(p, s, kin0 + 10 + n, A, Bx, win, o);
+      vol_step<MODE, T>(p, s, kin0 + 10 + n, pre, A, Bx, win, o);
       vol_consume<MODE, kNt, T>(p, s, s.k0 + n, o, dl, acc);
     }
   }
