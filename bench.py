@@ -81,7 +81,7 @@ def algorithmic_bytes(shape, padding, eb=4):
     both gradients (2 eb per element).  The recomputing kernels read x, y and
     write both gradients (4 eb per element); the inference forward reads x, y.
     With a cached reference: x, y and the cached map (4 B per map entry) in,
-    grad_x out."""
+    grad_x out; forming that map reads y and writes it."""
     N, C, H, W = shape
     Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
     e_in = N * C * H * W
@@ -91,7 +91,8 @@ def algorithmic_bytes(shape, padding, eb=4):
             "ssim_forward(inference)": 2 * eb * e_in,
             "ssim_backward_recompute": 4 * eb * e_in,
             "ssim_loss_and_grad": 4 * eb * e_in,
-            "ssim_loss_and_grad_ref": 3 * eb * e_in + 4 * e_out}
+            "ssim_loss_and_grad_ref": 3 * eb * e_in + 4 * e_out,
+            "ssim_reference_stats": eb * e_in + 4 * e_out}
 
 
 def algorithmic_flops(shape, padding):
@@ -159,10 +160,40 @@ def volume_algorithmic(shape, padding, eb):
     e_out = N * C * (D - sh) * (H - sh) * (W - sh)
     blur = 4 * 3 * 21
     by = {"ssim3d_forward": 2 * eb * e_in + 16 * e_out,
-          "ssim3d_backward": 16 * e_out + 4 * eb * e_in}
+          "ssim3d_backward": 16 * e_out + 4 * eb * e_in,
+          "ssim3d_forward(inference)": 2 * eb * e_in}
     fl = {"ssim3d_forward": 5 * e_in + (blur + 17 + 5 + 25) * e_out,
-          "ssim3d_backward": blur * e_in + 13 * e_in}
+          "ssim3d_backward": blur * e_in + 13 * e_in,
+          "ssim3d_forward(inference)": 5 * e_in + (blur + 17 + 5) * e_out}
     return by, fl
+
+
+def measured_traffic(args, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel of known
+    size), or None when there is none for this workload and dtype or it was
+    taken from another version of the kernel sources."""
+    tag = args.workload if args.dtype == "float32" else f"{args.workload}-{args.dtype}"
+    path = os.path.join(PROFILES, f"hbm_traffic_{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if (tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload
+            and tr.get("dtype", "float32") == args.dtype):
+        return tr.get("bytes_per_launch", {}).get(kernel)
+    return None
+
+
+def copy_calibration(mib, dev):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    import torch
+
+    a = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def bench_volume(args, w, x, y):
@@ -210,6 +241,8 @@ def bench_volume(args, w, x, y):
     kern = {"ssim3d_forward": per_launch_ms(fwd), "ssim3d_backward": per_launch_ms(bwd),
             "ssim3d_forward(inference)":
                 per_launch_ms(lambda: S.ssim3d_forward(t1, t2, w.padding, loss, None, ws))}
+    if args.copy_calib > 0:
+        copy_calibration(args.copy_calib, dev)
     by, fl = volume_algorithmic(x.shape, w.padding, eb)
     dom = max(("ssim3d_forward", "ssim3d_backward"), key=lambda k: kern[k])
     gbs = by[dom] / (kern[dom] * 1e-3) / 1e9
@@ -235,7 +268,8 @@ def bench_volume(args, w, x, y):
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": by[dom]},
                      "alu": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
-                             "algorithmic_flops": fl[dom]}},
+                             "algorithmic_flops": fl[dom]},
+                     "traffic": measured_traffic(args, dom)},
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "loss": float(loss.item()),
         "cpu_baseline": None,
@@ -358,12 +392,7 @@ def main():
         cold = {"ms_per_step": round(cms, 5), "mpix_per_s": round(mpix / (cms * 1e-3), 1)}
 
     if args.copy_calib > 0:
-        n = args.copy_calib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+        copy_calibration(args.copy_calib, dev)
 
     alg = algorithmic_bytes((N, C, H, W), w.padding, eb)
     flops = algorithmic_flops((N, C, H, W), w.padding)
@@ -378,16 +407,7 @@ def main():
     # HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
     # WRITE_SIZE, scaled by a copy kernel of known size), valid only for the
     # kernel source they were taken from
-    traffic = None
-    tag = args.workload if args.dtype == "float32" else f"{args.workload}-{args.dtype}"
-    traffic_file = os.path.join(PROFILES, f"hbm_traffic_{tag}.json")
-    if os.path.exists(traffic_file):
-        with open(traffic_file) as f:
-            tr = json.load(f)
-        if (tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload
-                and tr.get("dtype", "float32") == args.dtype
-                and dom in tr.get("bytes_per_launch", {})):
-            traffic = tr["bytes_per_launch"][dom]
+    traffic = measured_traffic(args, dom)
 
     # every design whose launches were all timed: its step from the per-kernel
     # times, and its algorithmic HBM rate
