@@ -9,12 +9,14 @@
 // with off = 0 / 5 (forward, valid / same) and 10 / 5 (backward, the adjoint).
 //
 // One workgroup (256 lanes) owns a 16 x 16 tile of output (i, j) positions of
-// one volume and marches along depth.  Per depth step it stages the 26 x 26
-// input tile of one slice in LDS (loaded one step ahead into registers), runs the X pass (26 x 16 partial sums) and
-// the Y pass (16 x 16) through LDS, and each lane shifts its four XY-blurred
-// values into an 11-deep register window whose 11-tap sum is the Z pass (a
-// shift keeps the register indices fixed without unrolling the depth loop,
-// whose per-step invariants would otherwise be hoisted and spilled).
+// one volume and marches along depth.  Each input slice is staged as a
+// 26 x 26 tile in LDS (loaded one step ahead into registers), blurred in X
+// (26 x 16 partial sums, through LDS) and in Y (16 x 16), and each lane
+// shifts its four XY-blurred values into an 11-deep register window whose
+// 11-tap sum is the Z pass (a shift keeps the register indices fixed without
+// unrolling the depth loop, whose per-step invariants would otherwise be
+// hoisted and spilled).  The three LDS stages of consecutive slices are
+// software-pipelined over double-buffered tiles, one barrier per slice.
 //
 // Training forward: the loss partials m0..m3 (ssim_device.hpp) are saved at
 // every map voxel, four planes per volume; the backward blurs them with the
@@ -29,9 +31,11 @@ namespace ssim_dev {
 
 constexpr int kVT = 16;           // output tile side (i and j)
 constexpr int kVIn = kVT + 10;    // input tile side
-constexpr int kVInP = kVIn + 1;   // LDS row pitch of the input tile
+constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
 constexpr int kVMinSlices = 24;   // shortest depth range of one workgroup
 static_assert(kVT * kVT == kThreads, "one output position per lane");
+static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
+              "X-pass tasks read whole 16-byte words inside a tile row");
 
 struct VolParams {
   int D, H, W;          // volume extent
@@ -148,37 +152,48 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
   }
 }
 
-// One depth step on input slice kin, whose tile `pre` holds: store it to LDS,
-// issue the loads of slice kin + 1 into `pre` (their latency hides behind
-// this step), blur in X and Y, shift the lane's window down by one slice with
-// the new values in slot 10, and return the Z-pass sum over slots 0 .. 10 in
-// o.
-template <int MODE, int T>
-__device__ __forceinline__ void vol_step(const VolParams& p, const VolSeg& s, int kin,
-                                         VolPre<MODE>& pre, float (&A)[kQ][kVIn][kVInP],
-                                         float (&Bx)[kQ][kVIn][kVT], float (&win)[11][kQ],
-                                         float (&o)[kQ]) {
-  vol_store<MODE>(pre, A);
-  vol_load<MODE, T>(p, s, kin + 1, pre);
-  __syncthreads();
-  // X pass: 26 rows x 16 columns of partial sums
-  constexpr int kXIters = (kVIn * kVT + kThreads - 1) / kThreads;
+// X pass of one staged slice: 26 rows x 16 columns of partial sums.  A task
+// is 4 adjacent outputs of one quantity in one row, formed from 16 columns
+// read as four 16-byte words; consecutive lanes take consecutive rows, so with
+// the 28-float row pitch any 8 (or 16) of them read distinct bank groups.
+constexpr int kXTasks = kQ * (kVT / 4) * kVIn;
+__device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
+                                          float (&Bx)[kQ][kVIn][kVT]) {
 #pragma unroll
-  for (int it = 0; it < kXIters; ++it) {
+  for (int it = 0; it < (kXTasks + kThreads - 1) / kThreads; ++it) {
     const int t = threadIdx.x + it * kThreads;
-    if (t < kVIn * kVT) {
-      const int r = t / kVT, c = t % kVT;
+    if (t < kXTasks) {
+      const int q = t / ((kVT / 4) * kVIn);
+      const int rem = t - q * ((kVT / 4) * kVIn);
+      const int g = rem / kVIn, r = rem - g * kVIn;
+      const float* src = &A[q][r][4 * g];
+      float v[16];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        float a = tap(0) * A[q][r][c];
-#pragma unroll
-        for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), A[q][r][c + b], a);
-        Bx[q][r][c] = a;
+      for (int k = 0; k < 4; ++k) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+        v[4 * k + 0] = f.x;
+        v[4 * k + 1] = f.y;
+        v[4 * k + 2] = f.z;
+        v[4 * k + 3] = f.w;
       }
+      float o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a = tap(0) * v[u];
+#pragma unroll
+        for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
+        o[u] = a;
+      }
+      *reinterpret_cast<float4*>(&Bx[q][r][4 * g]) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
-  __syncthreads();
-  // Y pass at this lane's (i, j), then the Z window
+}
+
+// Y pass at this lane's (i, j) of one X-blurred slice; the result enters the
+// lane's depth window in slot 10 (the window shifts down by one slice), and
+// o is the Z-pass sum over slots 0 .. 10.
+__device__ __forceinline__ void vol_ypass_z(const float (&Bx)[kQ][kVIn][kVT], float (&win)[11][kQ],
+                                            float (&o)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
   for (int k = 0; k < 10; ++k)
@@ -200,30 +215,48 @@ __device__ __forceinline__ void vol_step(const VolParams& p, const VolSeg& s, in
   }
 }
 
-// Consume the four blurred values of output slice k at this lane's (i, j).
-template <int MODE, bool kNt, int T>
-__device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s, int k,
-                                            const float (&o)[kQ], float dl, double& acc) {
+// Where output slice k at this lane's (i, j) lives: its element offset in
+// bytes for elements of eb bytes, or kOob outside the output extent.
+__device__ __forceinline__ unsigned vol_out_off(const VolParams& p, const VolSeg& s, int k,
+                                                unsigned eb) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
   const int i = s.i0 + ty, j = s.j0 + tx;
   const bool ok = (unsigned)k < (unsigned)p.out_d && i < p.out_h && j < p.out_w;
-  const unsigned e = ok ? (unsigned)(((int64_t)k * p.out_h + i) * p.out_w + j) : 0u;
+  return ok ? (unsigned)(((int64_t)k * p.out_h + i) * p.out_w + j) * eb : kOob;
+}
+
+// Backward: x and y at output slice k of this lane (issued a step before the
+// chain rule needs them).
+template <int T>
+__device__ __forceinline__ void vol_load_xy(const VolParams& p, const VolSeg& s, int k,
+                                            float (&xy)[2]) {
+  const unsigned off = vol_out_off(p, s, k, img_bytes<T>());
+  xy[0] = ld_img<T>(s.img[0], off);
+  xy[1] = ld_img<T>(s.img[1], off);
+}
+
+// Consume the four blurred values of output slice k at this lane's (i, j):
+// forward, the loss term and (training) the saved partials; backward, the
+// chain rule with this voxel's x, y (xy) and both gradients.
+template <int MODE, bool kNt, int T>
+__device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s, int k,
+                                            const float (&o)[kQ], const float (&xy)[2], float dl,
+                                            double& acc) {
   if constexpr (MODE == kBwd) {
-    constexpr unsigned kEb = img_bytes<T>();
-    const unsigned off = ok ? e * kEb : kOob;
-    const float xv = ld_img<T>(s.img[0], off), yv = ld_img<T>(s.img[1], off);
+    const unsigned off = vol_out_off(p, s, k, img_bytes<T>());
+    const float xv = xy[0], yv = xy[1];
     const float xs = xv - kShift, ys = yv - kShift, d = xv - yv;
     const float g1 = dl * __builtin_fmaf(d, o[2], __builtin_fmaf(ys, o[3], o[0]));
     const float g2 = dl * __builtin_fmaf(-d, o[2], __builtin_fmaf(xs, o[3], o[1]));
     st_img<T, kNt>(s.out[0], off, g1);
     st_img<T, kNt>(s.out[1], off, g2);
   } else {
+    const unsigned off = vol_out_off(p, s, k, 4u);
     const SsimTerms st = ssim_terms(o[0], o[1], o[2], o[3]);
-    acc += ok ? (double)one_minus_ssim(st) : 0.0;
+    acc += off != kOob ? (double)one_minus_ssim(st) : 0.0;
     if constexpr (MODE == kFwdTrain) {
       float m[4];
       loss_partials(o[0], o[1], st, p.k_m2, m);
-      const unsigned off = ok ? e * 4u : kOob;
 #pragma unroll
       for (int q = 0; q < kQ; ++q) st1<kNt>(s.out[q], off, m[q]);
     }
@@ -232,8 +265,8 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
 
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
-  __shared__ float A[kQ][kVIn][kVInP];
-  __shared__ float Bx[kQ][kVIn][kVT];
+  __shared__ __align__(16) float A[2][kQ][kVIn][kVInP];
+  __shared__ __align__(16) float Bx[2][kQ][kVIn][kVT];
   __shared__ double red[kWaves];
   __shared__ int is_last;
   constexpr unsigned kEb = img_bytes<T>();
@@ -270,21 +303,43 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       }
     }
 
-    // warm-up: input slices k0 - off .. k0 - off + 9 enter the window; output
-    // slice k0 + n then takes input slices kin0 + n .. kin0 + n + 10
+    // Input slices kin0 .. kin0 + nsl - 1 pass through the lane's depth
+    // window; the first 10 only fill it, and slice kin0 + 10 + n completes
+    // output slice k0 + n.  Three stages per slice, one step apart, each
+    // step ending in the only barrier: in step j the tile of slice j goes
+    // into A[j & 1] (its loads were issued in step j - 1), slice j - 1 is
+    // blurred in X from A[(j - 1) & 1] into Bx[(j - 1) & 1], and slice j - 2
+    // in Y from Bx[j & 1], then in Z.  No buffer is written in the step that
+    // reads its other use, and each stage reads what an earlier step wrote.
     float win[11][kQ];
 #pragma unroll
     for (int k = 0; k < 11; ++k)
 #pragma unroll
       for (int q = 0; q < kQ; ++q) win[k][q] = 0.0f;
-    float o[kQ];
     const int kin0 = s.k0 - p.off;
+    const int nsl = 10 + s.nk;
     VolPre<MODE> pre;
     vol_load<MODE, T>(p, s, kin0, pre);
-    for (int k = 0; k < 10; ++k) vol_step<MODE, T>(p, s, kin0 + k, pre, A, Bx, win, o);
-    for (int n = 0; n < s.nk; ++n) {
-      vol_step<MODE, T>(p, s, kin0 + 10 + n, pre, A, Bx, win, o);
-      vol_consume<MODE, kNt, T>(p, s, s.k0 + n, o, dl, acc);
+    float xy[2] = {0.0f, 0.0f};
+    for (int j = 0; j < nsl + 2; ++j) {
+      if (j < nsl) {
+        vol_store<MODE>(pre, A[j & 1]);
+        vol_load<MODE, T>(p, s, kin0 + j + 1, pre);
+      }
+      if (j >= 1 && j <= nsl) vol_xpass(A[(j - 1) & 1], Bx[(j - 1) & 1]);
+      if (j >= 2) {
+        float o[kQ];
+        vol_ypass_z(Bx[j & 1], win, o);
+        const int n = j - 12;  // output slice k0 + n, once the window is full
+        if (n >= 0) {
+          vol_consume<MODE, kNt, T>(p, s, s.k0 + n, o, xy, dl, acc);
+        }
+      }
+      // the chain rule's x, y for the next step's output slice
+      if constexpr (MODE == kBwd) {
+        if (j >= 11 && j < nsl + 1) vol_load_xy<T>(p, s, s.k0 + j - 11, xy);
+      }
+      __syncthreads();
     }
   }
   if constexpr (MODE != kBwd) {
