@@ -12,11 +12,11 @@
 // one volume and marches along depth.  Each input slice is staged as a
 // 26 x 26 tile in LDS (loaded one step ahead into registers), blurred in X
 // (26 x 16 partial sums, through LDS) and in Y (16 x 16), and each lane
-// shifts its four XY-blurred values into an 11-deep register window whose
-// 11-tap sum is the Z pass (a shift keeps the register indices fixed without
-// unrolling the depth loop, whose per-step invariants would otherwise be
-// hoisted and spilled).  The three LDS stages of consecutive slices are
-// software-pipelined over double-buffered tiles, one barrier per slice.
+// feeds its four XY-blurred values to 11 running sums per quantity that form
+// the Z pass (each sum moves one tap per slice inside its multiply-add, so
+// the register indices stay fixed without unrolling the depth loop).  The
+// three LDS stages of consecutive slices are software-pipelined over
+// double-buffered tiles, one barrier per slice.
 //
 // Training forward: the loss partials m0..m3 (ssim_device.hpp) are saved at
 // every map voxel, four planes per volume; the backward blurs them with the
@@ -189,29 +189,30 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
   }
 }
 
-// Y pass at this lane's (i, j) of one X-blurred slice; the result enters the
-// lane's depth window in slot 10 (the window shifts down by one slice), and
-// o is the Z-pass sum over slots 0 .. 10.
-__device__ __forceinline__ void vol_ypass_z(const float (&Bx)[kQ][kVIn][kVT], float (&win)[11][kQ],
-                                            float (&o)[kQ]) {
+// Y pass at this lane's (i, j) of one X-blurred slice.
+__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVIn][kVT], float (&a)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
-  for (int k = 0; k < 10; ++k)
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) win[k][q] = win[k + 1][q];
-#pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    float a = tap(0) * Bx[q][ty][tx];
+    float s = tap(0) * Bx[q][ty][tx];
 #pragma unroll
-    for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), Bx[q][ty + b][tx], a);
-    win[10][q] = a;
+    for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), Bx[q][ty + b][tx], s);
+    a[q] = s;
   }
+}
+
+// Z pass as running sums: acc[c] holds the partial sum, over the slices seen
+// so far, of the output whose window has the newest slice at tap c.  Each new
+// XY-blurred value a moves every sum one tap on, acc[c] <- acc[c - 1] +
+// g[c] a (the multiply-add writes the moved sum, so no register is copied),
+// and acc[10] is then the complete sum, in tap order, of the output whose
+// window ends at the new slice.
+__device__ __forceinline__ void vol_zpass(float (&acc)[11][kQ], const float (&a)[kQ]) {
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    float a = tap(0) * win[0][q];
 #pragma unroll
-    for (int c = 1; c < 11; ++c) a = __builtin_fmaf(tap(c), win[c][q], a);
-    o[q] = a;
+    for (int c = 10; c > 0; --c) acc[c][q] = __builtin_fmaf(tap(c), a[q], acc[c - 1][q]);
+    acc[0][q] = tap(0) * a[q];
   }
 }
 
@@ -303,19 +304,19 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       }
     }
 
-    // Input slices kin0 .. kin0 + nsl - 1 pass through the lane's depth
-    // window; the first 10 only fill it, and slice kin0 + 10 + n completes
+    // Input slices kin0 .. kin0 + nsl - 1 pass through the lane's running
+    // sums; the first 10 only start them, and slice kin0 + 10 + n completes
     // output slice k0 + n.  Three stages per slice, one step apart, each
     // step ending in the only barrier: in step j the tile of slice j goes
     // into A[j & 1] (its loads were issued in step j - 1), slice j - 1 is
     // blurred in X from A[(j - 1) & 1] into Bx[(j - 1) & 1], and slice j - 2
     // in Y from Bx[j & 1], then in Z.  No buffer is written in the step that
     // reads its other use, and each stage reads what an earlier step wrote.
-    float win[11][kQ];
+    float acc_z[11][kQ];
 #pragma unroll
     for (int k = 0; k < 11; ++k)
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) win[k][q] = 0.0f;
+      for (int q = 0; q < kQ; ++q) acc_z[k][q] = 0.0f;
     const int kin0 = s.k0 - p.off;
     const int nsl = 10 + s.nk;
     VolPre<MODE> pre;
@@ -327,14 +328,13 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
         vol_load<MODE, T>(p, s, kin0 + j + 1, pre);
       }
       if (j >= 1 && j <= nsl) vol_xpass(A[(j - 1) & 1], Bx[(j - 1) & 1]);
-      if (j >= 2) {
-        float o[kQ];
-        vol_ypass_z(Bx[j & 1], win, o);
-        const int n = j - 12;  // output slice k0 + n, once the window is full
-        if (n >= 0) {
-          vol_consume<MODE, kNt, T>(p, s, s.k0 + n, o, xy, dl, acc);
-        }
-      }
+      // (before slice 0 reaches the Y pass the sums take zeros, which leave
+      // them unchanged but keep their update out of any branch)
+      float a[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (j >= 2) vol_ypass(Bx[j & 1], a);
+      vol_zpass(acc_z, a);
+      const int n = j - 12;  // output slice k0 + n, once its 11 slices are in
+      if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, acc_z[10], xy, dl, acc);
       // the chain rule's x, y for the next step's output slice
       if constexpr (MODE == kBwd) {
         if (j >= 11 && j < nsl + 1) vol_load_xy<T>(p, s, s.k0 + j - 11, xy);
