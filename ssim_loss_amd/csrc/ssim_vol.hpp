@@ -32,7 +32,7 @@ namespace ssim_dev {
 constexpr int kVT = 16;           // output tile side (i and j)
 constexpr int kVIn = kVT + 10;    // input tile side
 constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
-constexpr int kVMinSlices = 24;   // shortest depth range of one workgroup
+constexpr int kVMinSlices = 16;   // shortest depth range of one workgroup
 static_assert(kVT * kVT == kThreads, "one output position per lane");
 static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
               "X-pass tasks read whole 16-byte words inside a tile row");
