@@ -29,6 +29,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -119,10 +121,22 @@ def algorithmic_flops(shape, padding):
             "ssim_loss_and_grad": recompute + 5 * e_out, "ssim_loss_and_grad_ref": ref_step}
 
 
-def cpu_baseline(x, y, padding, pixels_per_image_batch):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(x, y, padding, pixels_per_image_batch, dloss):
     """The fp64 oracle, as it stands, on the host cores: whole forward +
     gradient of the same workload, repeated until about 10 s have passed
-    (at most 200 times)."""
+    (at most 200 times); then one image plane on a single thread.  Returns
+    the baseline record and the oracle's last (loss, grad_x, grad_y)."""
     import oracle
 
     try:
@@ -133,19 +147,31 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch):
     oracle.set_threads(threads)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.ssim_loss(x, y, padding)
+        res = oracle.ssim_loss(x, y, padding, dloss=dloss)
         reps += 1
         el = time.perf_counter() - t0
         if el >= 10.0 or reps >= 200:
             break
-    return {
+    # one (n, c) plane on one thread: a pixel of the batch has C planes
+    C = x.shape[1]
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    oracle.ssim_loss(x[:1, :1], y[:1, :1], padding, dloss=dloss)
+    el1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
+    plane_pixels = x.shape[2] * x.shape[3]
+    record = {
         "value": round(reps * pixels_per_image_batch / el / 1e6, 3),
         "unit": "Mpix/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{reps} x whole forward+gradient of the benchmark batch "
                   f"({x.shape}, {padding}) in {el:.1f} s",
+        "single_thread": {"value": round(plane_pixels / C / el1 / 1e6, 3), "unit": "Mpix/s",
+                          "sample": f"one {x.shape[2]}x{x.shape[3]} plane in {el1:.2f} s"},
+        "cpu_model": cpu_model(),
     }
+    return record, res
 
 
 def volume_algorithmic(shape, padding, eb):
@@ -469,7 +495,24 @@ def main():
         "loss": float(loss.item()),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x, y, w.padding, N * H * W)
+        # the oracle gets the values the GPU read (half-precision inputs rounded)
+        xo = t1.float().cpu().numpy()
+        yo = t2.float().cpu().numpy()
+        # one fresh step of the timed design, for parity against the oracle
+        g1.zero_()
+        g2.zero_()
+        step()
+        torch.cuda.synchronize()
+        dl = float(dloss.item())
+        out["cpu_baseline"], (ol, ogx, ogy) = cpu_baseline(xo, yo, w.padding, N * H * W, dl)
+        gl = float(loss.item())
+        par = {"loss_rel_err": abs(gl - ol) / abs(ol),
+               "grad1_err_over_max": float(np.abs(g1.float().cpu().numpy() - ogx).max()
+                                           / np.abs(ogx).max())}
+        if args.design != "one-pass-ref":
+            par["grad2_err_over_max"] = float(np.abs(g2.float().cpu().numpy() - ogy).max()
+                                              / np.abs(ogy).max())
+        out["parity_vs_oracle"] = {k: float(f"{v:.3g}") for k, v in par.items()}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

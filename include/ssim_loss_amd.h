@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 5
+#define SSIM_ABI_VERSION 6
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -96,10 +96,10 @@ int ssim_map_shape(int64_t H, int64_t W, int padding, int64_t* Ho, int64_t* Wo);
  * aligned.  Returns 0 for invalid arguments.  Host-only. */
 size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding);
 
-/* Bytes of the workspace ssim_forward needs (a per-workgroup partial-sum
- * table and a completion counter).  The caller zero-fills it once, before
- * its first use; every ssim_forward leaves it ready for the next call (the
- * last workgroup resets the counter).  One workspace must not be used by
+/* Bytes of the workspace ssim_forward needs (the loss reduction's
+ * accumulator: a fixed-point sum and a completion count in one 64-bit word).
+ * The caller zero-fills it once, before its first use; every ssim_forward
+ * leaves it ready for the next call (the last workgroup resets it).  One workspace must not be used by
  * two ssim_forward calls that may run at the same time.  Host-only. */
 size_t ssim_workspace_bytes(void);
 
@@ -189,7 +189,7 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
  *   grad_img1/2  : device outputs of `dtype`, or NULL to skip
  *   stream       : hipStream_t (NULL = default stream)
  * Deterministic, like ssim_forward; the loss equals ssim_forward's up to the
- * order of the fp64 summation. */
+ * rounding of the summation (the two kernels split the map differently). */
 int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
                        int64_t H, int64_t W, int padding, const float* dloss, float* loss,
                        void* workspace, void* grad_img1, void* grad_img2, void* stream);

@@ -70,9 +70,9 @@
 //
 // Loss reduction: the map entries of 1 - S are summed as per-lane fp32 sums
 // of 4 outputs -> fp64 per lane -> wave64 shuffle tree -> LDS -> one fp64
-// partial per workgroup -> the last workgroup (completion ticket) sums the
-// partials in a fixed order and writes loss = sum / M.  Deterministic; no
-// atomics on floating point.
+// partial per workgroup -> one 64-bit atomic add of the partial in fixed
+// point together with a completion count (finish_loss); the last workgroup
+// writes loss = sum / M.  Deterministic; no atomics on floating point.
 
 #pragma once
 
@@ -96,7 +96,7 @@ constexpr int kRowLanes = kStripOut / 4;  // lanes active in the row pass (61)
 constexpr int kRows = 4;         // rows per batch = waves (one row each in the row pass)
 constexpr int kRing = 12;        // ring slots: 11 rows needed, 12 so 3 batches of 4 close the cycle
 constexpr int kQ = 4;            // blurred quantities / maps
-constexpr int kMaxBlocks = 4096; // bound on the grid (size of the partial-sum table)
+constexpr int kMaxBlocks = 4096; // bound on the grid
 constexpr int kMinRowsPerBlock = 8;
 
 static_assert(kRows == kWaves, "row pass maps one batch row per wave");
@@ -128,10 +128,11 @@ constexpr float kC1 = 1.0e-4f;  // (0.01 * 1)^2
 constexpr float kC2 = 9.0e-4f;  // (0.03 * 1)^2
 constexpr float kShift = 0.5f;  // x' = x - 1/2 (see the file header)
 
+// The loss reduction's accumulator (finish_loss): fixed-point sum and
+// completion count in one word, zero between launches.
 struct Workspace {
-  unsigned int ticket;
-  unsigned int pad[63];
-  double partial[kMaxBlocks];
+  unsigned long long acc;
+  unsigned long long pad[31];
 };
 
 // kRef: blur a reference image alone and store its blurred mean B(y - 1/2)
@@ -565,11 +566,21 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
 
 // Workgroup sum of the map of 1 - S, then the last workgroup to finish
 // forms the mean: loss = sum / M.  Every thread of the workgroup calls it.
+//
+// One 64-bit word carries both the running sum and the completion count:
+// each workgroup adds (round(partial * 2^F) << T) + 1 with a single atomic,
+// T = the bit length of the grid size (so the count never carries into the
+// sum) and F = 62 - T - ceil(log2(2M)) (every partial is at most 2 per map
+// entry, so the sum stays inside the word's 63 - T signed bits).  The
+// workgroup whose add brings the count to the grid size holds the whole sum
+// in the returned value: one round trip to memory, and no other value has
+// to be published or ordered.  Integer addition is exact and associative,
+// so the loss is the same bits on every run; the fixed point's rounding is at
+// most G 2^-(F+1) on the sum, about 2^(2T - 62) / loss relative to the loss.
 template <int kNW>
-__device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kNW],
-                                            int& is_last) {
+__device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kNW]) {
   const int tid = threadIdx.x;
-  const int G = gridDim.x;
+  const unsigned G = gridDim.x;
   const int wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
@@ -579,27 +590,18 @@ __device__ __forceinline__ void finish_loss(const Params& p, double acc, double 
     double bs = 0.0;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) bs += red[w];
-    // Publish the partial with a device-coherent atomic store and wait for
-    // its acknowledgement before taking the ticket: a release of exactly
-    // this one value.  (A release fence would also write back every dirty
-    // line of this XCD's L2 -- megabytes of map stores -- in every
-    // workgroup.)
-    __hip_atomic_store(&p.ws->partial[blockIdx.x], bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    const unsigned prev =
-        __hip_atomic_fetch_add(&p.ws->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (unsigned)(G - 1));
-  }
-  __syncthreads();
-  if (is_last && wave == 0) {
-    double sum = 0.0;
-    for (int k = lane; k < G; k += kWave)
-      sum += __hip_atomic_load(&p.ws->partial[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-    if (lane == 0) {
-      *p.loss = (float)(sum * p.inv_m);
-      __hip_atomic_store(&p.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int T = 32 - __clz((int)G);  // 2^T > G
+    int e;
+    frexp(2.0 / p.inv_m, &e);           // 2M < 2^e
+    const int F = 62 - T - e;
+    const unsigned long long q = (unsigned long long)__double2ll_rn(ldexp(bs, F));
+    const unsigned long long add = (q << T) + 1ull;
+    const unsigned long long now =
+        __hip_atomic_fetch_add(&p.ws->acc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    if ((now & ((1ull << T) - 1ull)) == G) {
+      const long long total = (long long)now >> T;  // the count is G < 2^T: no borrow
+      *p.loss = (float)(ldexp((double)total, -F) * p.inv_m);
+      __hip_atomic_store(&p.ws->acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -642,7 +644,6 @@ template <int MODE, bool kVec, bool kNt, int T>
 __device__ __forceinline__ void strip_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kTileW];
   __shared__ double red[kWaves];
-  __shared__ int is_last;
 
   const int tid = threadIdx.x;
   // Every workgroup gets the same amount of work, so the grid (one resident
@@ -720,7 +721,7 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     }
   }
 
-  if constexpr (MODE == kFwdInfer || MODE == kFwdTrain) finish_loss<kWaves>(p, acc, red, is_last);
+  if constexpr (MODE == kFwdInfer || MODE == kFwdTrain) finish_loss<kWaves>(p, acc, red);
 }
 
 }  // namespace ssim_dev

@@ -387,7 +387,6 @@ template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false>
 __device__ __forceinline__ void fused_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kFTileW];
   __shared__ double red[kFWaves];
-  __shared__ int is_last;
 
   // wave index as a scalar, so the split below is a scalar branch: each wave
   // runs exactly one of the two loops
@@ -459,7 +458,7 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       gb += nb;
     }
   }
-  if constexpr (kLoss) finish_loss<kFWaves>(p, acc, red, is_last);
+  if constexpr (kLoss) finish_loss<kFWaves>(p, acc, red);
 }
 
 }  // namespace ssim_dev

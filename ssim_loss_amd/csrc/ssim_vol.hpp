@@ -269,7 +269,6 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
   __shared__ __align__(16) float A[2][kQ][kVIn][kVInP];
   __shared__ __align__(16) float Bx[2][kQ][kVIn][kVT];
   __shared__ double red[kWaves];
-  __shared__ int is_last;
   constexpr unsigned kEb = img_bytes<T>();
 
   float dl = 0.0f;
@@ -348,7 +347,7 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     q.ws = p.ws;
     q.loss = p.loss;
     q.inv_m = p.inv_m;
-    finish_loss<kWaves>(q, acc, red, is_last);
+    finish_loss<kWaves>(q, acc, red);
   }
 }
 
