@@ -46,12 +46,21 @@ constexpr int kFGradLanes = kFOut / 4;              // stage-2 row-pass lanes (5
 constexpr int kFTileW = kTileW + 4;                 // 256 lanes + the last lane's 4-column overhang
 constexpr int kFThreads = 2 * kThreads;             // two groups of 4 waves, one per stage
 constexpr int kFWaves = kFThreads / kWave;
+// Rows of x and y kept in LDS between the two stages: stage 2 needs image
+// row r for the chain rule 14 to 17 rows after stage 1 loaded it, and stage 1
+// writes 4 new rows per tick, so 20 slots hold every row until its last use
+// and are never written in the tick that reads them.
+constexpr int kXYRing = 20;
+constexpr int kXYOff = 2;  // column t at index t + 2: stage 2's 4-column groups start 16-byte aligned
 
 static_assert(kFMapCols + 10 == kTileW, "a strip's image columns are one per lane");
 static_assert(4 * (kFMapLanes - 1) + 16 <= kFTileW, "stage-1 row-pass reads stay in the tile row");
 static_assert(4 * (kFGradLanes - 1) + 16 <= 4 * kFMapLanes,
               "stage-2 row-pass reads stay in the columns stage 1 wrote");
 static_assert(kFOut % 4 == 0 && (kFTileW * 4) % 16 == 0, "16-byte aligned tile rows and groups");
+static_assert(kXYOff + kTileW <= kFTileW && (kXYOff + 10) % 4 == 0,
+              "the row ring holds a strip row; gradient groups read it 16-byte aligned");
+static_assert(kXYRing % kRows == 0 && kXYRing >= 18, "ring depth covers the stage-1 to stage-2 lag");
 
 struct FSeg {
   rsrc_t img[2];        // x, y planes
@@ -133,6 +142,7 @@ __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ
 template <bool kLoss, int T, int PH, bool kRef>
 __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
+                                             float (&xyr)[kXYRing][2][kFTileW],
                                              float (&ring)[kRing][kQ], float (&pre)[kRows][2],
                                              int t, int buf, int col, int wave, int lane,
                                              double& acc) {
@@ -150,6 +160,14 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
 #pragma unroll
   for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + 4 * (t + 1) + m, pre[m]);
 
+  // this batch's rows of x and y, kept for stage 2's chain rule (ring slot
+  // = row within the range mod kXYRing)
+  const int xslot = kRows * (t % (kXYRing / kRows));
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) {
+    xyr[xslot + m][0][col + kXYOff] = cur[m][0];
+    xyr[xslot + m][1][col + kXYOff] = cur[m][1];
+  }
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
     constexpr int kB0 = 4 * PH;
@@ -228,16 +246,16 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
 template <bool kVec, bool kNt, int T, int PH, bool kRef>
 __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
+                                             const float (&xyr)[kXYRing][2][kFTileW],
                                              float (&ring)[kRing][kQ], int t, int buf, int col,
                                              int wave, int lane, float dl) {
   // with a cached reference only grad_x is formed: m1 (which feeds grad_y
   // alone) is neither blurred nor used
   constexpr int kSkip = kRef ? 1 : -1;
   constexpr unsigned kEb = img_bytes<T>();
-  // the gradient row this wave finishes, and its images for the chain rule
-  // (loaded first, so their latency hides behind the column pass).  Memory
-  // operations are never under a branch: groups that are not real use
-  // out-of-range offsets (loads give 0, stores are dropped).
+  // the gradient row this wave finishes; its x and y come from the row ring
+  // that stage 1 filled (no second read of the images).  Stores are never
+  // under a branch: groups that are not real use out-of-range offsets.
   const int gr = 4 * t + wave - 10;  // row within the range; < 0 while the adjoint warms up
   const bool grow = gr >= 0 && gr < s.nrows;
   const int gv = s.v0 + 4 * lane;
@@ -246,17 +264,6 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   unsigned goff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) goff[c] = (gok && gv + c < p.img_w) ? gbase + kEb * c : kOob;
-  float xv[4], yv[4];
-  if constexpr (kVec) {
-    ld_img4<T>(s.img[0], gbase, xv);
-    ld_img4<T>(s.img[1], gbase, yv);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      xv[c] = ld_img<T>(s.img[0], goff[c]);
-      yv[c] = ld_img<T>(s.img[1], goff[c]);
-    }
-  }
 
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
@@ -281,6 +288,11 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   float g1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (grow) {
     const int lr = lane < kFGradLanes ? lane : kFGradLanes - 1;
+    // stage-1 lane 10 + 4 lr + c held image column v0 + 4 lr + c
+    const float4 xq = *reinterpret_cast<const float4*>(&xyr[gr % kXYRing][0][4 * lr + 10 + kXYOff]);
+    const float4 yq = *reinterpret_cast<const float4*>(&xyr[gr % kXYRing][1][4 * lr + 10 + kXYOff]);
+    const float xv[4] = {xq.x, xq.y, xq.z, xq.w};
+    const float yv[4] = {yq.x, yq.y, yq.z, yq.w};
     float o[kQ][4];
     row_pass<kSkip>(&tile[buf][0][wave][0], 4 * lr, o);
 #pragma unroll
@@ -386,6 +398,7 @@ __device__ __forceinline__ int segment_batches(const FSeg& s) {
 template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false>
 __device__ __forceinline__ void fused_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kFTileW];
+  __shared__ float xyr[kXYRing][2][kFTileW];
   __shared__ double red[kFWaves];
 
   // wave index as a scalar, so the split below is a scalar branch: each wave
@@ -415,13 +428,13 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       }
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
                                           acc);
         ++t;
       }
@@ -448,11 +461,11 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       __syncthreads();
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage2_batch<kVec, kNt, T, 0, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 0, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 1, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 1, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 2, kRef>(p, s, tile, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 2, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         ++t;
       }
       gb += nb;
