@@ -571,12 +571,14 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
 // each workgroup adds (round(partial * 2^F) << T) + 1 with a single atomic,
 // T = the bit length of the grid size (so the count never carries into the
 // sum) and F = 62 - T - ceil(log2(2M)) (every partial is at most 2 per map
-// entry, so the sum stays inside the word's 63 - T signed bits).  The
-// workgroup whose add brings the count to the grid size holds the whole sum
-// in the returned value: one round trip to memory, and no other value has
-// to be published or ordered.  Integer addition is exact and associative,
-// so the loss is the same bits on every run; the fixed point's rounding is at
-// most G 2^-(F+1) on the sum, about 2^(2T - 62) / loss relative to the loss.
+// entry, so the whole sum stays below bit 62).  The workgroup whose add
+// brings the count to the grid size holds the whole sum in the returned
+// value: one round trip to memory, and no other value has to be published or
+// ordered.  Integer addition is exact and associative, so the loss is the
+// same bits on every run; the fixed point's rounding is at most G 2^-(F+1) on
+// the sum, about 2^(2T - 62) / loss relative to the loss.  A partial that is
+// not finite or not below that bound (NaN or infinite inputs) sets bit 63
+// with an atomic OR completed before its add, and the loss is then NaN.
 template <int kNW>
 __device__ __forceinline__ void finish_loss(const Params& p, double acc, double (&red)[kNW]) {
   const int tid = threadIdx.x;
@@ -594,13 +596,23 @@ __device__ __forceinline__ void finish_loss(const Params& p, double acc, double 
     int e;
     frexp(2.0 / p.inv_m, &e);           // 2M < 2^e
     const int F = 62 - T - e;
-    const unsigned long long q = (unsigned long long)__double2ll_rn(ldexp(bs, F));
+    const double scaled = ldexp(bs, F);
+    constexpr unsigned long long kPoison = 1ull << 63;
+    if (!(fabs(scaled) < ldexp(1.0, 62 - T))) {  // also true for NaN
+      __hip_atomic_fetch_or(&p.ws->acc, kPoison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    // rounding may leave a partial of zero slightly negative: it adds 0
+    const unsigned long long q =
+        scaled > 0.0 && scaled < ldexp(1.0, 62 - T) ? (unsigned long long)__double2ll_rn(scaled)
+                                                    : 0ull;
     const unsigned long long add = (q << T) + 1ull;
     const unsigned long long now =
         __hip_atomic_fetch_add(&p.ws->acc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
     if ((now & ((1ull << T) - 1ull)) == G) {
-      const long long total = (long long)now >> T;  // the count is G < 2^T: no borrow
-      *p.loss = (float)(ldexp((double)total, -F) * p.inv_m);
+      const unsigned long long total = (now & ~kPoison) >> T;
+      *p.loss = (now & kPoison) ? __builtin_nanf("")
+                                : (float)(ldexp((double)total, -F) * p.inv_m);
       __hip_atomic_store(&p.ws->acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

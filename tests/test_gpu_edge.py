@@ -201,6 +201,62 @@ def test_workspace_reuse_across_shapes():
         check_loss(gl, ol)
 
 
+def test_non_finite_input_gives_nan_loss_and_leaves_the_workspace_ready():
+    """A NaN or infinite pixel makes the loss NaN (as the plain definition
+    does) in every loss-forming kernel: the strip forward (training and
+    inference), the one-launch step, the cached-reference step and the volume
+    forward.  The reduction's accumulator is reset either way, so the next
+    call on the same workspace is exact again."""
+    import math
+
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    ws = S.workspace_for(dev)
+    x, y = make_pair((2, 3, 70, 300), "uniform", 0.1, seed=91)
+    ol, _, _ = oracle.ssim_loss(x, y, "valid", grads=False)
+    t2 = torch.from_numpy(y).to(dev)
+    ref = S.reference_stats(t2, "valid")
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dl = torch.tensor(1.0, device=dev)
+    g1 = torch.empty_like(t2)
+    g2 = torch.empty_like(t2)
+    maps = S.alloc_saved_maps(t2, "valid")
+    runs = {
+        "forward": lambda a: S.ssim_forward(a, t2, "valid", loss, maps, ws),
+        "forward(inference)": lambda a: S.ssim_forward(a, t2, "valid", loss, None, ws),
+        "loss_and_grad": lambda a: S.ssim_loss_and_grad(a, t2, "valid", dl, loss, ws, g1, g2),
+        "loss_and_grad_ref": lambda a: S.ssim_loss_and_grad_ref(a, t2, ref, "valid", dl, loss,
+                                                                ws, g1),
+    }
+    for bad in (float("nan"), float("inf")):
+        xb = x.copy()
+        xb[1, 2, 33, 150] = bad
+        tb = torch.from_numpy(xb).to(dev)
+        tx = torch.from_numpy(x).to(dev)
+        for name, run in runs.items():
+            say(f"  {name} with {bad}")
+            run(tb)
+            torch.cuda.synchronize()
+            assert math.isnan(float(loss.item())), name
+            run(tx)
+            torch.cuda.synchronize()
+            check_loss(float(loss.item()), ol, name)
+    xv, yv = make_pair((1, 2, 20, 19, 18), "uniform", 0.1, seed=92)
+    ov, _, _ = oracle.ssim3_loss(xv, yv, "same", grads=False)
+    tv2 = torch.from_numpy(yv).to(dev)
+    xvb = xv.copy()
+    xvb[0, 1, 7, 8, 9] = float("nan")
+    S.ssim3d_forward(torch.from_numpy(xvb).to(dev), tv2, "same", loss, None, ws)
+    torch.cuda.synchronize()
+    assert math.isnan(float(loss.item())), "ssim3d_forward"
+    S.ssim3d_forward(torch.from_numpy(xv).to(dev), tv2, "same", loss, None, ws)
+    torch.cuda.synchronize()
+    check_loss(float(loss.item()), ov, "ssim3d_forward")
+
+
 def test_rejects_bad_inputs_on_gpu():
     import torch
 
