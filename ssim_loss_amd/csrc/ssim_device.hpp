@@ -327,19 +327,21 @@ __device__ __forceinline__ float one_minus_ssim(const SsimTerms& t) {
 //   m1 = -(1/M) dS/dmu_y' = k (mu_x T1 - mu_x' T2 - T3)
 //   m2 = -(2/M) dS/dR     = -k S B1   (the chain rule's 2 folded in)
 //   m3 = -(1/M) dS/dP'    = k T2
+// Every product carries k inv = k_m2 inv^2 =: a once, so with X = a A1,
+// Y = a A2: k T2 = X D2 B1, k T1 = Y D1 B2, k T3 = X A2 (B1 - B2) dmu and
+// k S B1 = X A2 B1.  A zero k_m2 gives four zero partials.
 __device__ __forceinline__ void loss_partials(float mxs, float mys, const SsimTerms& t, float k_m2,
                                               float (&m)[4]) {
-  const float s = t.a1 * t.a2 * t.inv;
-  const float ib1 = t.b2 * t.inv;
-  const float ib2 = t.b1 * t.inv;
-  const float t1 = t.a2 * t.d1 * ib1;
-  const float t2 = t.a1 * t.d2 * ib2;
-  const float t3 = s * (t.b1 - t.b2) * t.dm;
-  const float k = k_m2 * t.inv;
-  m[0] = k * __builtin_fmaf(t.muy, t1, __builtin_fmaf(-mys, t2, t3));
-  m[1] = k * __builtin_fmaf(t.mux, t1, __builtin_fmaf(-mxs, t2, -t3));
-  m[2] = -(k * s) * t.b1;
-  m[3] = k * t2;
+  const float a = k_m2 * t.inv * t.inv;
+  const float X = a * t.a1, Y = a * t.a2;
+  const float xa2 = X * t.a2;
+  const float kt2 = X * t.d2 * t.b1;
+  const float kt1 = Y * t.d1 * t.b2;
+  const float kt3 = xa2 * ((t.b1 - t.b2) * t.dm);
+  m[0] = __builtin_fmaf(t.muy, kt1, __builtin_fmaf(-mys, kt2, kt3));
+  m[1] = __builtin_fmaf(t.mux, kt1, __builtin_fmaf(-mxs, kt2, -kt3));
+  m[2] = -xa2 * t.b1;
+  m[3] = kt2;
 }
 
 // ---------------------------------------------------------------------------

@@ -214,9 +214,11 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
       const bool in_map = (unsigned)jm < (unsigned)p.map_w && jl < kFMapCols;
       const SsimTerms st = ssim_terms(o[0][c], o[1][c], o[2][c], o[3][c]);
       float m4[4];
-      loss_partials(o[0][c], o[1][c], st, p.k_m2, m4);
+      // outside the map the partials are the adjoint's zero fill (a zero
+      // scale: every input of the row pass is finite, the overhang included)
+      loss_partials(o[0][c], o[1][c], st, in_map ? p.k_m2 : 0.0f, m4);
 #pragma unroll
-      for (int k = 0; k < kQ; ++k) part[k][c] = in_map ? m4[k] : 0.0f;
+      for (int k = 0; k < kQ; ++k) part[k][c] = m4[k];
       if constexpr (kLoss) {
         const float ell = one_minus_ssim(st);
         s4 += (own_row && in_map && lane < kFMapLanes && jm < s.own_c1) ? ell : 0.0f;
@@ -405,6 +407,13 @@ __device__ __forceinline__ void fused_body(const Params& p) {
   // runs exactly one of the two loops
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
+  // the tile rows' 4-column overhang past the 256 lanes is read by the last
+  // stage-1 row-pass lane but written by no stage: zero it once, so that
+  // the entries it feeds (outside the map) stay finite and scale to zero
+  if (threadIdx.x < 2 * kQ * kRows * (kFTileW - kTileW)) {
+    const int k = threadIdx.x % (kFTileW - kTileW), r = threadIdx.x / (kFTileW - kTileW);
+    (&tile[0][0][0][0])[r * kFTileW + kTileW + k] = 0.0f;
+  }
   FShare w = fused_share(p);
   double acc = 0.0;
   int gb = 0;  // batches of earlier segments
