@@ -24,7 +24,9 @@
 //             entries per lane: 236 gradient columns per strip.
 // Row pipeline: image row r enters stage 1; it completes map row
 // r + off - 10, whose partials complete gradient row r - 10 in stage 2.  A
-// row range of n gradient rows therefore reads n + 20 image rows.  Map
+// row range of n gradient rows therefore reads n + 20 image rows, each once:
+// stage 1 also keeps the rows it loads in an LDS ring, from which stage 2
+// takes x and y for the chain rule.  Map
 // entries shared by two strips or two row ranges are computed by both, and
 // the loss counts each exactly once, in the strip and range that own it.
 //
