@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -66,12 +67,23 @@ def parse():
     return ap.parse_args()
 
 
+_CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
+
+
 def source_hash() -> str:
-    """Hash of the library's sources (every file under csrc/, in name order)."""
+    """Hash of the library's code (every file under csrc/ and include/, in
+    name order), with comments dropped and white space collapsed: counters
+    taken from a kernel stay valid across edits that do not change its code."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    inc = os.path.join(ROOT, "include")
+    paths = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))]
+    paths += [os.path.join(inc, n) for n in sorted(os.listdir(inc))]
+    for path in paths:
+        name = os.path.basename(path)
+        with open(path, encoding="utf-8") as f:
+            src = f.read()
+        code = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+        h.update(name.encode() + b"\0" + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
