@@ -152,13 +152,17 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
   }
 }
 
-// X pass of one staged slice: 26 rows x 16 columns of partial sums.  A task
-// is 4 adjacent outputs of one quantity in one row, formed from 16 columns
-// read as four 16-byte words; consecutive lanes take consecutive rows, so with
-// the 28-float row pitch any 8 (or 16) of them read distinct bank groups.
+// X pass of one staged slice: 26 rows x 16 columns of partial sums, stored
+// column-major (Bx[q][column][row]).  A task is 4 adjacent outputs of one
+// quantity in one row, formed from 16 columns read as four 16-byte words;
+// consecutive lanes take consecutive rows, so with the 28-float row pitch
+// any 8 (or 16) of them read distinct bank groups, and their 4 single-word
+// stores land on consecutive words.  The Y pass then reads 11 consecutive
+// words per lane, and the 26-word column pitch spreads a half-wave's 16
+// columns x 2 rows over 32 distinct banks.
 constexpr int kXTasks = kQ * (kVT / 4) * kVIn;
 __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
-                                          float (&Bx)[kQ][kVIn][kVT]) {
+                                          float (&Bx)[kQ][kVT][kVIn]) {
 #pragma unroll
   for (int it = 0; it < (kXTasks + kThreads - 1) / kThreads; ++it) {
     const int t = threadIdx.x + it * kThreads;
@@ -184,19 +188,20 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
         for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
         o[u] = a;
       }
-      *reinterpret_cast<float4*>(&Bx[q][r][4 * g]) = make_float4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Bx[q][4 * g + u][r] = o[u];
     }
   }
 }
 
 // Y pass at this lane's (i, j) of one X-blurred slice.
-__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVIn][kVT], float (&a)[kQ]) {
+__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVIn], float (&a)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    float s = tap(0) * Bx[q][ty][tx];
+    float s = tap(0) * Bx[q][tx][ty];
 #pragma unroll
-    for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), Bx[q][ty + b][tx], s);
+    for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), Bx[q][tx][ty + b], s);
     a[q] = s;
   }
 }
@@ -267,7 +272,7 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
   __shared__ __align__(16) float A[2][kQ][kVIn][kVInP];
-  __shared__ __align__(16) float Bx[2][kQ][kVIn][kVT];
+  __shared__ __align__(16) float Bx[2][kQ][kVT][kVIn];
   __shared__ double red[kWaves];
   constexpr unsigned kEb = img_bytes<T>();
 
