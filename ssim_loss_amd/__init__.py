@@ -273,14 +273,17 @@ _workspaces: dict = {}
 
 
 def workspace_for(device) -> "torch.Tensor":
-    """A zero-initialised workspace per device, created once.  Calls that use
-    it must not overlap in time (one stream per device, as torch's default)."""
+    """A zero-initialised workspace per (device, current stream), created once
+    (zeroed on that stream, so before its first use there).  Calls on one
+    stream run in order, so they may share it; calls on different streams get
+    different workspaces and may overlap."""
     import torch
 
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.zeros(ssim_workspace_bytes(), dtype=torch.uint8, device=key)
+        ws = torch.zeros(ssim_workspace_bytes(), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 

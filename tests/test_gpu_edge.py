@@ -201,6 +201,40 @@ def test_workspace_reuse_across_shapes():
         check_loss(gl, ol)
 
 
+def test_two_streams_get_their_own_workspaces():
+    """Loss-forming calls on two streams may overlap: the binding keeps one
+    workspace per (device, stream), and each stream's losses stay exact."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    pairs = [make_pair((2, 3, 150, 400), "uniform", 0.1, seed=70 + k) for k in range(2)]
+    refs = [oracle.ssim_loss(x, y, "same", grads=False)[0] for x, y in pairs]
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    data = []
+    for (x, y), st in zip(pairs, streams):
+        with torch.cuda.stream(st):
+            t1 = torch.from_numpy(x).to(dev)
+            t2 = torch.from_numpy(y).to(dev)
+            data.append((t1, t2, torch.empty((), dtype=torch.float32, device=dev),
+                         torch.empty_like(t1), torch.empty_like(t2), S.workspace_for(dev)))
+    assert data[0][5].data_ptr() != data[1][5].data_ptr()
+    torch.cuda.synchronize()
+    dl = torch.tensor(1.0, device=dev)
+    losses = [[], []]
+    for _ in range(5):
+        for k, st in enumerate(streams):
+            t1, t2, loss, g1, g2, _ = data[k]
+            with torch.cuda.stream(st):
+                S.ssim_loss_and_grad(t1, t2, "same", dl, loss, S.workspace_for(dev), g1, g2)
+                losses[k].append(loss.clone())
+    torch.cuda.synchronize()
+    for k in range(2):
+        for v in losses[k]:
+            check_loss(float(v.item()), refs[k], f"stream {k}")
+
+
 def test_non_finite_input_gives_nan_loss_and_leaves_the_workspace_ready():
     """A NaN or infinite pixel makes the loss NaN (as the plain definition
     does) in every loss-forming kernel: the strip forward (training and
