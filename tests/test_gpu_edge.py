@@ -235,6 +235,61 @@ def test_two_streams_get_their_own_workspaces():
             check_loss(float(v.item()), refs[k], f"stream {k}")
 
 
+def test_graph_capture_replays_match_eager():
+    """A training step captured in a HIP graph (the one-launch kernel, and the
+    saved-maps forward + backward pair) replays with new image contents each
+    time, with eager work and synchronisations between replays, and every
+    replay equals the eager launches bit for bit.  The kernels record no
+    memset: the loss accumulator resets itself."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    shape = (2, 3, 120, 333)
+    t1 = torch.empty(shape, dtype=torch.float32, device=dev)
+    t2 = torch.empty_like(t1)
+    g1, g2, e1, e2 = (torch.empty_like(t1) for _ in range(4))
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    loss_e = torch.empty_like(loss)
+    dl = torch.tensor(0.7, device=dev)
+    ws = torch.zeros(S.ssim_workspace_bytes(), dtype=torch.uint8, device=dev)
+    ws_e = torch.zeros_like(ws)
+    maps = S.alloc_saved_maps(t1, "valid")
+    steps = {
+        "one launch": lambda w, l, a, b: S.ssim_loss_and_grad(t1, t2, "valid", dl, l, w, a, b),
+        "saved maps": lambda w, l, a, b: (S.ssim_forward(t1, t2, "valid", l, maps, w),
+                                          S.ssim_backward(dl, t1, t2, "valid", maps, a, b)),
+    }
+    for name, step in steps.items():
+        x, y = make_pair(shape, "uniform", 0.1, seed=80)
+        t1.copy_(torch.from_numpy(x))
+        t2.copy_(torch.from_numpy(y))
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step(ws, loss, g1, g2)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(ws, loss, g1, g2)
+        for k in range(4):
+            say(f"  {name}: replay {k}")
+            x, y = make_pair(shape, "uniform", 0.05 + 0.05 * k, seed=81 + k)
+            t1.copy_(torch.from_numpy(x))
+            t2.copy_(torch.from_numpy(y))
+            graph.replay()
+            torch.cuda.synchronize()
+            step(ws_e, loss_e, e1, e2)
+            torch.cuda.synchronize()
+            assert float(loss.item()) == float(loss_e.item()), (name, k)
+            assert torch.equal(g1, e1) and torch.equal(g2, e2), (name, k)
+            if k == 0:
+                ol, _, _ = oracle.ssim_loss(x, y, "valid", grads=False)
+                check_loss(float(loss.item()), ol, name)
+
+
 def test_non_finite_input_gives_nan_loss_and_leaves_the_workspace_ready():
     """A NaN or infinite pixel makes the loss NaN (as the plain definition
     does) in every loss-forming kernel: the strip forward (training and
