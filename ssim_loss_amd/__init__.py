@@ -42,6 +42,10 @@ import threading
 
 from .build import LIB_PATH
 
+# SSIM_ABI_VERSION of include/ssim_loss_amd.h that these bindings follow; a
+# library built from another version is refused at load time
+ABI_VERSION = 6
+
 PAD = {"valid": 0, "same": 1}
 SSIM_OK = 0
 SSIM_DTYPE = {"float32": 0, "float16": 1, "bfloat16": 2}
@@ -72,6 +76,10 @@ def lib() -> ctypes.CDLL:
         i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
         L.ssim_abi_version.restype = i32
         L.ssim_abi_version.argtypes = []
+        if L.ssim_abi_version() != ABI_VERSION:
+            raise ImportError(
+                f"{LIB_PATH} implements ABI version {L.ssim_abi_version()}, these bindings "
+                f"version {ABI_VERSION}: rebuild it")
         L.ssim_strerror.restype = ctypes.c_char_p
         L.ssim_strerror.argtypes = [i32]
         L.ssim_taps.restype = None

@@ -39,7 +39,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert S.ssim_abi_version() == 6
+    # the header, the built library and the bindings agree on the version
+    hdr = open(HEADER).read()
+    v = int(re.search(r"#define SSIM_ABI_VERSION (\d+)", hdr).group(1))
+    assert S.ssim_abi_version() == v == S.ABI_VERSION
     for code in range(0, -9, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
@@ -237,3 +240,13 @@ def test_python_binding_rejects_cpu_tensors():
         S.ssim_loss(x.double(), x.double())
     with pytest.raises(TypeError):
         S.ssim_loss(x.half(), x.half())
+
+
+def test_build_entry_point_compiles_and_checks_the_abi():
+    """__graft_entry__.build() compiles the library and the oracle in-tree
+    (the atomic rename leaves the copy this process loaded intact) and checks
+    the built library's ABI version against the bindings."""
+    import importlib
+
+    entry = importlib.import_module("__graft_entry__")
+    entry.build()
