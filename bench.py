@@ -9,16 +9,20 @@ current stream:
               ssim_backward (both image gradients)
   recompute : ssim_forward (inference: loss only), then
               ssim_backward_recompute (both gradients, no maps)
+  one-pass-ref : ssim_loss_and_grad_ref (a fixed reference whose statistics
+              were cached outside the step; grad_img1 only)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--dtype float32|float16|bfloat16] [--design NAME] [--all-kernels]
+                    [--dtype float32|float16|bfloat16] [--design NAME]
+                    [--no-all-kernels] [--no-cpu]
 
 Prints one JSON line: metric Mpix/s (pixels = N*H*W per step, wall clock over
 K steps), the roofline of the dominant kernel (algorithmic bytes per launch /
 average launch time from HIP events around K back-to-back launches of that
-kernel on the stream it runs on), per-design step times when their kernels
-were timed, and the fp64 CPU oracle's throughput on a bounded sample of the
-same workload.
+kernel on the stream it runs on), every design's step time from its kernels'
+times (unless --no-all-kernels), the fp64 CPU oracle's throughput on a
+bounded sample of the same workload and the parity of the timed step against
+it.  Volume workloads (vol-*) time ssim3d_forward + ssim3d_backward instead.
 """
 from __future__ import annotations
 
@@ -57,8 +61,9 @@ def parse():
                          "one-pass: loss and gradients in one launch; "
                          "one-pass-ref: the same with the reference's statistics cached and "
                          "only the first image's gradient")
-    ap.add_argument("--all-kernels", action="store_true",
-                    help="also time the kernels of the other designs")
+    ap.add_argument("--all-kernels", action=argparse.BooleanOptionalAction, default=True,
+                    help="after the timed steps, also time the kernels of the other designs "
+                         "(reported under 'designs'; on by default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with a cache flush before each (0 = skip)")
