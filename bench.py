@@ -437,10 +437,29 @@ def main():
     if args.copy_calib > 0:
         copy_calibration(args.copy_calib, dev)
 
+    # a plain device copy moving the dominant kernel's algorithmic bytes
+    # (half read, half written), for the HBM fraction against what a copy of
+    # that size reaches on this device
+    def copy_gbs(nbytes):
+        n = max(1, int(nbytes // 8))
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        return 8.0 * n / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
     alg = algorithmic_bytes((N, C, H, W), w.padding, eb)
     flops = algorithmic_flops((N, C, H, W), w.padding)
     dom = max(DESIGNS[args.design], key=lambda k: kern[k])
     achieved = alg[dom] / (kern[dom] * 1e-3) / 1e9
+    cgbs = copy_gbs(alg[dom])
     achieved_tf = flops[dom] / (kern[dom] * 1e-3) / 1e12
     # the bound of the dominant kernel: the resource it uses the larger
     # fraction of (the saved-maps kernels stream HBM; the recomputing ones
@@ -509,6 +528,12 @@ def main():
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "designs": designs,
         "cold": cold,
+        "rates": {
+            "melem_per_s": round(N * C * H * W * K / elapsed / 1e6, 1),
+            "gbs_at_24_b_per_elem": round(24 * N * C * H * W * K / elapsed / 1e9, 1),
+            "copy_gbs_same_bytes": round(cgbs, 1),
+            "hbm_frac_of_copy": round(achieved / cgbs, 4),
+        },
         "loss": float(loss.item()),
     }
     if not args.no_cpu:
