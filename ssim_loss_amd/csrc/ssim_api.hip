@@ -311,8 +311,15 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   p.off2 = padding == SSIM_PAD_VALID ? 10 : 5;  // map -> gradient (the adjoint)
   p.map_h = (int)s.Ho;
   p.map_w = (int)s.Wo;
-  p.strips = (int)((s.W + kFOut - 1) / kFOut);
-  p.cols = s.planes * p.strips;
+  // the planes side by side, each followed by a gap of at least 10 zero
+  // columns (the halo of either padding), a plane pitch of at least 256 (a
+  // strip's 256 lanes then touch at most two planes) and a multiple of 4
+  // (4-column groups stay inside one plane or one gap)
+  int64_t vp = s.W + 10 > 256 ? s.W + 10 : 256;
+  vp = (vp + 3) / 4 * 4;
+  p.vpitch = (int)vp;
+  p.planes = s.planes;
+  p.cols = ((s.planes - 1) * vp + s.W + kFOut - 1) / kFOut;
   p.x = img1;
   p.y = img2;
   p.img_plane = s.H * s.W;

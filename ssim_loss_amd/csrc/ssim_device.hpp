@@ -178,9 +178,15 @@ struct Params {
   void* gx;             // of the kernel's image type
   void* gy;
   // recomputing kernels (image -> map -> gradient in one pass): off is the
-  // forward's offset, off2 the adjoint's; the map extent
+  // forward's offset, off2 the adjoint's; the map extent.  Their strips run
+  // over the planes laid side by side, plane p's columns starting at virtual
+  // column p * vpitch (vpitch >= W + 10 and >= 256, a multiple of 4: the gap
+  // reads as zeros, and a strip spans at most two planes); cols counts
+  // those strips.
   int off2;
   int map_h, map_w;
+  int vpitch;
+  int64_t planes;
 };
 
 // ---------------------------------------------------------------------------

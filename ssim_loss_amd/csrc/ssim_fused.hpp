@@ -65,24 +65,59 @@ static_assert(kXYOff + kTileW <= kFTileW && (kXYOff + 10) % 4 == 0,
 static_assert(kXYRing % kRows == 0 && kXYRing >= 18, "ring depth covers the stage-1 to stage-2 lag");
 
 struct FSeg {
-  rsrc_t img[2];        // x, y planes
-  rsrc_t out[2];        // grad_x, grad_y planes (zero-size when not wanted)
-  unsigned colbyte;     // this lane's image column (stage 1), bytes, or kOob
+  rsrc_t img[2];        // x, y from plane p0 on (at most two planes)
+  rsrc_t out[2];        // grad_x, grad_y from plane p0 (zero-size when not wanted)
+  unsigned colbyte;     // this lane's image column (stage 1): byte offset from plane p0, or kOob
   unsigned row_bytes;   // image row pitch, bytes
+  unsigned plane_bytes; // image plane, bytes
+  int img_h;            // image rows
   int u0, nrows;        // gradient rows [u0, u0 + nrows)
-  int v0;               // first gradient column of the strip
-  int jm0;              // first map column of the strip: v0 - off2
+  int rv0;              // first gradient column of the strip, relative to plane p0's column 0
+  bool p1;              // plane p0 + 1 exists
+  bool last;            // the last strip: it owns the map columns right of its own range
   int i0;               // map row completed by the first batch row: u0 - off2
-  int own_r1;           // the loss counts map rows [i0, own_r1) ...
-  int own_c1;           // ... and map columns [jm0, own_c1) (clipped to the map)
-  rsrc_t ref;           // cached reference statistics: B(y - 1/2) map plane
-  unsigned ref_row;     // its row pitch, bytes
+  int own_r1;           // the loss counts map rows [i0, own_r1)
+  rsrc_t ref;           // cached reference statistics: B(y - 1/2) map planes from p0
+  unsigned ref_row;     // their row pitch, bytes
+  unsigned ref_plane;   // their plane, bytes
 };
+
+// Where relative column rc (from plane p0's column 0) lies: its offset in
+// bytes of eb-byte elements from plane p0's start (plane p0 or p0 + 1), or
+// kOob for the gap between planes, left of the first and right of the last.
+__device__ __forceinline__ unsigned plane_col(const Params& p, const FSeg& s, int rc, int w,
+                                              unsigned plane_bytes, unsigned eb) {
+  if ((unsigned)rc < (unsigned)w) return (unsigned)rc * eb;
+  const int r2 = rc - p.vpitch;
+  return (s.p1 && (unsigned)r2 < (unsigned)w) ? plane_bytes + (unsigned)r2 * eb : kOob;
+}
+
+// Per segment and row-pass lane: bit c (c < 4) when the lane's map entry c
+// lies in a map (outside, the partials are the adjoint's zero fill), bit
+// 4 + c when this strip also owns it for the loss (its own 236 map columns,
+// and everything to the right for the last strip; rows are checked per
+// batch).
+__device__ __forceinline__ unsigned fused_masks(const Params& p, const FSeg& s, int lane) {
+  const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
+  unsigned mk = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int jl = 4 * lr + c;  // map column within the strip
+    const bool in_map =
+        jl < kFMapCols && plane_col(p, s, s.rv0 - p.off2 + jl, p.map_w, 0u, 1u) != kOob;
+    const bool own = in_map && lane < kFMapLanes && (jl < kFOut || s.last);
+    mk |= (in_map ? 1u << c : 0u) | (own ? 1u << (4 + c) : 0u);
+  }
+  return mk;
+}
 
 // This lane's pixel of x and y in image row r (0 outside the image).
 template <int T>
 __device__ __forceinline__ void fload_row(const FSeg& s, int r, float (&v)[2]) {
-  const unsigned off = s.colbyte + (unsigned)r * s.row_bytes;
+  // rows outside the image are checked here: with two planes behind one
+  // descriptor, a row past one plane's edge would be a valid offset into the
+  // other
+  const unsigned off = (unsigned)r < (unsigned)s.img_h ? s.colbyte + (unsigned)r * s.row_bytes : kOob;
   v[0] = ld_img<T>(s.img[0], off);
   v[1] = ld_img<T>(s.img[1], off);
 }
@@ -146,8 +181,8 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              float (&xyr)[kXYRing][2][kFTileW],
                                              float (&ring)[kRing][kQ], float (&pre)[kRows][2],
-                                             int t, int buf, int col, int wave, int lane,
-                                             double& acc) {
+                                             unsigned mk, int t, int buf, int col, int wave,
+                                             int lane, double& acc) {
   constexpr int kSkip = kRef ? 1 : -1;  // with a cached reference, B(y') is read, not blurred
   const int i = s.i0 + 4 * t + wave;
   const bool irow = (unsigned)i < (unsigned)p.map_h;
@@ -194,9 +229,8 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
     // the cached B(y - 1/2) at this lane's 4 map entries (0 outside the map)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int jm = s.jm0 + 4 * lr + c;
-      const bool ok = irow && (unsigned)jm < (unsigned)p.map_w;
-      muy_ref[c] = ld1(s.ref, ok ? (unsigned)i * s.ref_row + (unsigned)jm * 4u : kOob);
+      const unsigned cb = plane_col(p, s, s.rv0 - p.off2 + 4 * lr + c, p.map_w, s.ref_plane, 4u);
+      muy_ref[c] = ld1(s.ref, irow && cb != kOob ? (unsigned)i * s.ref_row + cb : kOob);
     }
   }
   float part[kQ][4];
@@ -211,9 +245,7 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
     float s4 = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int jl = 4 * lr + c;  // map column within the strip
-      const int jm = s.jm0 + jl;
-      const bool in_map = (unsigned)jm < (unsigned)p.map_w && jl < kFMapCols;
+      const bool in_map = (mk >> c) & 1u;
       const SsimTerms st = ssim_terms(o[0][c], o[1][c], o[2][c], o[3][c]);
       float m4[4];
       // outside the map the partials are the adjoint's zero fill (a zero
@@ -223,7 +255,7 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
       for (int k = 0; k < kQ; ++k) part[k][c] = m4[k];
       if constexpr (kLoss) {
         const float ell = one_minus_ssim(st);
-        s4 += (own_row && in_map && lane < kFMapLanes && jm < s.own_c1) ? ell : 0.0f;
+        s4 += (own_row && ((mk >> (4 + c)) & 1u)) ? ell : 0.0f;
       }
     }
     if constexpr (kLoss) acc += (double)s4;
@@ -262,12 +294,17 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   // under a branch: groups that are not real use out-of-range offsets.
   const int gr = 4 * t + wave - 10;  // row within the range; < 0 while the adjoint warms up
   const bool grow = gr >= 0 && gr < s.nrows;
-  const int gv = s.v0 + 4 * lane;
-  const bool gok = grow && lane < kFGradLanes && gv < p.img_w;
-  const unsigned gbase = gok ? (unsigned)(s.u0 + gr) * s.row_bytes + (unsigned)gv * kEb : kOob;
+  // (with W and the plane pitch multiples of 4 a vector group lies wholly in
+  // one plane or wholly in a gap, so its first column decides)
+  const int gc = s.rv0 + 4 * lane;  // relative column of the lane's first gradient
+  const unsigned rowoff = (unsigned)(s.u0 + gr) * s.row_bytes;
   unsigned goff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) goff[c] = (gok && gv + c < p.img_w) ? gbase + kEb * c : kOob;
+  for (int c = 0; c < 4; ++c) {
+    const unsigned cb = plane_col(p, s, gc + c, p.img_w, s.plane_bytes, kEb);
+    goff[c] = (grow && lane < kFGradLanes && cb != kOob) ? rowoff + cb : kOob;
+  }
+  const unsigned gbase = goff[0];
 
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
@@ -355,30 +392,35 @@ __device__ __forceinline__ bool next_segment(const Params& p, FShare& w, FSeg& s
     const int row_end = (int)(r1 > 0 ? r1 : 0);
     w.v = seg_end;
     if (row_end <= row_begin) continue;
-    const int64_t plane = sc / p.strips;
-    const int strip = (int)(sc - plane * p.strips);
+    // strip sc of the planes laid side by side: plane p0 holds its first
+    // image column (the halo's), and it reaches at most plane p0 + 1
+    const int64_t v0 = sc * kFOut;
+    const int64_t p0 = v0 >= 10 ? (v0 - 10) / p.vpitch : 0;
+    const int64_t np = p.planes - p0 < 2 ? p.planes - p0 : 2;
     s.u0 = row_begin;
     s.nrows = row_end - row_begin;
-    s.v0 = strip * kFOut;
-    s.jm0 = s.v0 - p.off2;
+    s.rv0 = (int)(v0 - p0 * p.vpitch);
+    s.p1 = np > 1;
+    s.last = sc == p.cols - 1;
     s.i0 = s.u0 - p.off2;
-    const int c = s.v0 - 10 + col;
-    s.colbyte = (c >= 0 && c < p.img_w) ? (unsigned)c * kEb : kOob;
     s.row_bytes = (unsigned)p.img_w * kEb;
-    const int64_t pb = plane * p.img_plane * kEb;
-    s.img[0] = make_rsrc(byte_ptr(p.x, pb), p.img_plane * kEb);
-    s.img[1] = make_rsrc(byte_ptr(p.y, pb), p.img_plane * kEb);
-    s.out[0] = make_rsrc(p.gx ? byte_ptr(p.gx, pb) : p.x, p.gx ? p.img_plane * kEb : 0);
-    s.out[1] = make_rsrc(p.gy ? byte_ptr(p.gy, pb) : p.y, p.gy ? p.img_plane * kEb : 0);
-    // the last row range and the last strip own the map's remaining rows and
-    // columns (same padding: the map reaches 5 past the last gradient row
-    // range's own share)
+    s.plane_bytes = (unsigned)(p.img_plane * kEb);
+    s.img_h = p.in_h;
+    s.colbyte = plane_col(p, s, s.rv0 - 10 + col, p.img_w, s.plane_bytes, kEb);
+    const int64_t pb = p0 * p.img_plane * kEb;
+    const int64_t span = np * p.img_plane * kEb;
+    s.img[0] = make_rsrc(byte_ptr(p.x, pb), span);
+    s.img[1] = make_rsrc(byte_ptr(p.y, pb), span);
+    s.out[0] = make_rsrc(p.gx ? byte_ptr(p.gx, pb) : p.x, p.gx ? span : 0);
+    s.out[1] = make_rsrc(p.gy ? byte_ptr(p.gy, pb) : p.y, p.gy ? span : 0);
+    // the last row range owns the map's remaining rows (same padding: the map
+    // reaches 5 past the last gradient row range's own share)
     s.own_r1 = (row_end == p.out_h) ? p.map_h : row_end - p.off2;
-    s.own_c1 = (strip == p.strips - 1) ? p.map_w : s.jm0 + kFOut;
     // cached reference statistics (the map buffer with its row pitch), if any
-    s.ref = make_rsrc(p.maps ? p.maps + plane * p.map_plane : p.x,
-                      p.maps ? p.map_plane * 4 : 0);
+    s.ref = make_rsrc(p.maps ? p.maps + p0 * p.map_plane : p.x,
+                      p.maps ? np * p.map_plane * 4 : 0);
     s.ref_row = (unsigned)p.map_pitch * 4u;
+    s.ref_plane = (unsigned)(p.map_plane * 4);
     return true;
   }
 }
@@ -426,6 +468,7 @@ __device__ __forceinline__ void fused_body(const Params& p) {
     FSeg s;
     while (next_segment<T>(p, w, s, col)) {
       const int nb = segment_batches(s);
+      const unsigned mk = fused_masks(p, s, lane);
       float ring[kRing][kQ];
       float pre[kRows][2];
       {
@@ -439,13 +482,16 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       }
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+                                          lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+                                          lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, pre, t, (gb + t) & 1, col, wave_id, lane,
+        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+                                          lane,
                                           acc);
         ++t;
       }
