@@ -359,3 +359,59 @@ def test_rejects_bad_inputs_on_gpu():
         S.ssim_loss(a.transpose(2, 3), a)
     with pytest.raises(S.SsimError):
         S.ssim_loss(torch.rand(1, 1, 8, 32, device=dev), torch.rand(1, 1, 8, 32, device=dev), "valid")
+
+
+def test_maximum_plane_size():
+    """Two planes of 2^27 elements (8192 x 16384, the documented limit; 1 GiB
+    per tensor): the one-launch step (whose strips span both planes behind one
+    descriptor, offsets near 1 GiB) and the saved-maps pair, each against the
+    oracle's whole loss and its gradients at sampled pixels (corners, plane
+    edges, strip boundaries, random points)."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    shape = (2, 1, 8192, 16384)
+    N, C, H, W = shape
+    say(f"[edge] maximum plane {shape}")
+    x, y = make_pair(shape, "uniform", 0.05, seed=2027)
+    M = float(N * C * (H - 10) * (W - 10))
+    dloss = 0.9
+    dev = torch.device("cuda")
+    t1 = torch.from_numpy(x).to(dev)
+    t2 = torch.from_numpy(y).to(dev)
+    rng = np.random.default_rng(5)
+    pts = [(n, 0, u, v) for n in range(N) for u in (0, 1, H - 2, H - 1)
+           for v in (0, 9, 235, 236, W - 12, W - 1)]
+    pts += [(int(rng.integers(N)), 0, int(rng.integers(H)), int(rng.integers(W))) for _ in range(120)]
+    say("  oracle samples")
+    o1 = np.zeros(len(pts))
+    o2 = np.zeros(len(pts))
+    for k, (n, c, u, v) in enumerate(pts):
+        o1[k], o2[k] = oracle.sample_grad(x[n, c], y[n, c], "valid", M, dloss, u, v)
+    say("  oracle loss")
+    ol, _, _ = oracle.ssim_loss(x, y, "valid", grads=False)
+    idx = torch.tensor(pts, dtype=torch.long, device=dev)
+
+    def samples(g):
+        return g[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]].cpu().numpy().astype(np.float64)
+
+    say("  one launch")
+    loss, g1, g2 = S.loss_and_grad(t1, t2, "valid", weight=dloss)
+    torch.cuda.synchronize()
+    check_loss(float(loss.item()), ol, "one launch")
+    check_grad(samples(g1), o1, "one launch grad_img1")
+    check_grad(samples(g2), o2, "one launch grad_img2")
+    del g1, g2
+    say("  saved maps")
+    ws = S.workspace_for(dev)
+    maps = S.alloc_saved_maps(t1, "valid")
+    dl = torch.tensor(dloss, device=dev)
+    g1 = torch.empty_like(t1)
+    g2 = torch.empty_like(t2)
+    S.ssim_forward(t1, t2, "valid", loss, maps, ws)
+    S.ssim_backward(dl, t1, t2, "valid", maps, g1, g2)
+    torch.cuda.synchronize()
+    check_loss(float(loss.item()), ol, "saved maps")
+    check_grad(samples(g1), o1, "saved maps grad_img1")
+    check_grad(samples(g2), o2, "saved maps grad_img2")
