@@ -173,3 +173,32 @@ def test_volume_inference_identity_null_grads_and_autograd():
     assert abs(float(s.item()) - (1 - ol)) <= 1e-5 * abs(ol)
     check_grad(t1.grad.cpu().numpy(), og1, "autograd grad_vol1")
     assert t2.grad is None
+
+
+def test_volume_at_the_size_limit():
+    """One 512^3 volume pair (2^27 voxels, the documented limit; 512 MiB per
+    tensor), valid padding.  The volumes are constant along depth, so the
+    whole loss is the 2-D oracle's loss of one slice (the reduction the
+    volume oracle's pins establish); gradients at sampled voxels come from
+    the volume oracle one by one."""
+    import torch
+
+    n = 512
+    x2, y2 = make_pair((1, 1, n, n), "uniform", 0.05, seed=512)
+    x = np.ascontiguousarray(np.broadcast_to(x2[:, :, None], (1, 1, n, n, n)))
+    y = np.ascontiguousarray(np.broadcast_to(y2[:, :, None], (1, 1, n, n, n)))
+    say(f"[vol] size limit {x.shape}")
+    dloss = 1.1
+    gl, g1, g2 = vol_run(x, y, "valid", dloss=dloss, keep_on_device=True)
+    ol, _, _ = oracle.ssim_loss(x2, y2, "valid", grads=False)
+    check_loss(gl, ol, "512^3 volume")
+    M = float((n - 10) ** 3)
+    rng = np.random.default_rng(6)
+    pts = [(t, u, v) for t in (0, 5, n - 1) for u in (0, n - 1) for v in (0, 15, 16, n - 1)]
+    pts += [tuple(int(rng.integers(n)) for _ in range(3)) for _ in range(40)]
+    idx = torch.tensor(pts, dtype=torch.long, device=g1.device)
+    s1 = g1[0, 0, idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
+    s2 = g2[0, 0, idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
+    o = np.array([oracle.sample_grad3(x[0, 0], y[0, 0], "valid", M, dloss, t, u, v) for t, u, v in pts])
+    check_grad(s1, o[:, 0], "512^3 grad_vol1 samples")
+    check_grad(s2, o[:, 1], "512^3 grad_vol2 samples")
