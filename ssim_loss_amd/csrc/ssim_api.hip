@@ -396,7 +396,7 @@ int check_shape3(int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int padd
 // whole tile-columns.
 int launch_vol(const DeviceInfo* d, int dtype, int which, VolParams& p, void* stream) {
   p.tiles_x = (p.out_w + kVT - 1) / kVT;
-  p.tiles_y = (p.out_h + kVT - 1) / kVT;
+  p.tiles_y = (p.out_h + kVTy - 1) / kVTy;
   p.cols = p.cols * p.tiles_x * p.tiles_y;  // volumes * tiles
   int64_t resident = (int64_t)d->cus * d->occ[dtype][which];
   if (resident > kMaxBlocks) resident = kMaxBlocks;

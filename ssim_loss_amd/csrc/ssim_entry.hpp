@@ -37,7 +37,9 @@ enum KernelKind {
   kKinds
 };
 __host__ __device__ constexpr int kind_threads(int k) {
-  return (k >= kKRecomp && k <= kKLossGradRefUnaligned) ? kFThreads : kThreads;
+  return (k >= kKRecomp && k <= kKLossGradRefUnaligned) ? kFThreads
+         : k >= kKVolFwdInfer                           ? kVThreads
+                                                        : kThreads;
 }
 // the parameter block each kind takes
 __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdInfer; }
@@ -58,7 +60,7 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
 // LDS reads in flight; without an occupancy target the scheduler hoists
 // reads into registers far past that
 #define SSIM_VKERNEL_(NAME, WAVES, BODY)                                                   \
-  __global__ __launch_bounds__(ssim_dev::kThreads) __attribute__((amdgpu_waves_per_eu(WAVES))) \
+  __global__ __launch_bounds__(ssim_dev::kVThreads) __attribute__((amdgpu_waves_per_eu(WAVES))) \
   void NAME(const ssim_dev::VolParams p) {                                                 \
     BODY(p);                                                                               \
   }
@@ -96,9 +98,9 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
                (ssim_dev::strip_body<ssim_dev::kRef, false, false, T>))                    \
   SSIM_VKERNEL_(ssim3d_fwd_infer##NAME##kernel, 4,                                         \
                 (ssim_dev::vol_body<ssim_dev::kFwdInfer, false, T>))                        \
-  SSIM_VKERNEL_(ssim3d_fwd_train##NAME##kernel, 3,                                         \
+  SSIM_VKERNEL_(ssim3d_fwd_train##NAME##kernel, 4,                                         \
                 (ssim_dev::vol_body<ssim_dev::kFwdTrain, false, T>))                        \
-  SSIM_VKERNEL_(ssim3d_bwd##NAME##kernel, 3, (ssim_dev::vol_body<ssim_dev::kBwd, false, T>)) \
+  SSIM_VKERNEL_(ssim3d_bwd##NAME##kernel, 4, (ssim_dev::vol_body<ssim_dev::kBwd, false, T>)) \
   }                                                                                        \
   const void* const* TABLE() {                                                             \
     static const void* const t[ssim_dev::kKinds] = {                                      \

@@ -8,10 +8,10 @@
 //     out[k][i][j] = sum_{a,b,c} g[a] g[b] g[c] in[k+a-off][i+b-off][j+c-off],
 // with off = 0 / 5 (forward, valid / same) and 10 / 5 (backward, the adjoint).
 //
-// One workgroup (256 lanes) owns a 16 x 16 tile of output (i, j) positions of
+// One workgroup (512 lanes) owns a 32 x 16 tile of output (i, j) positions of
 // one volume and marches along depth.  Each input slice is staged as a
-// 26 x 26 tile in LDS (loaded one step ahead into registers), blurred in X
-// (26 x 16 partial sums, through LDS) and in Y (16 x 16), and each lane
+// 42 x 26 tile in LDS (loaded one step ahead into registers), blurred in X
+// (42 x 16 partial sums, through LDS) and in Y (32 x 16), and each lane
 // feeds its four XY-blurred values to 11 running sums per quantity that form
 // the Z pass (each sum moves one tap per slice inside its multiply-add, so
 // the register indices stay fixed without unrolling the depth loop).  The
@@ -29,11 +29,15 @@
 
 namespace ssim_dev {
 
-constexpr int kVT = 16;           // output tile side (i and j)
-constexpr int kVIn = kVT + 10;    // input tile side
+constexpr int kVT = 16;           // output tile columns (j)
+constexpr int kVTy = 32;          // output tile rows (i)
+constexpr int kVIn = kVT + 10;    // input tile columns
+constexpr int kVInY = kVTy + 10;  // input tile rows
 constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
+constexpr int kVThreads = kVT * kVTy;    // one output position per lane
+constexpr int kVWaves = kVThreads / kWave;
 constexpr int kVMinSlices = 16;   // shortest depth range of one workgroup
-static_assert(kVT * kVT == kThreads, "one output position per lane");
+static_assert(kVThreads % kWave == 0, "whole waves");
 static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
               "X-pass tasks read whole 16-byte words inside a tile row");
 
@@ -89,9 +93,9 @@ struct VolSeg {
 };
 
 // One slice's input tile, held in registers between its loads and its LDS
-// store: each lane owns up to kVIters positions of the 26 x 26 tile (the
+// store: each lane owns up to kVIters positions of the 42 x 26 tile (the
 // last iteration is partial).  Forward: x and y; backward: the 4 partials.
-constexpr int kVIters = (kVIn * kVIn + kThreads - 1) / kThreads;
+constexpr int kVIters = (kVInY * kVIn + kVThreads - 1) / kVThreads;
 template <int MODE>
 struct VolPre {
   float v[kVIters][MODE == kBwd ? 4 : 2];
@@ -109,8 +113,8 @@ __device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, in
   const bool kok = (unsigned)kin < (unsigned)p.in_d;
 #pragma unroll
   for (int it = 0; it < kVIters; ++it) {
-    const int t = threadIdx.x + it * kThreads;
-    const bool in_tile = t < kVIn * kVIn;
+    const int t = threadIdx.x + it * kVThreads;
+    const bool in_tile = t < kVInY * kVIn;
     const int tt = in_tile ? t : 0;
     const int r = tt / kVIn, c = tt - r * kVIn;
     const int ii = s.i0 - p.off + r, jj = s.j0 - p.off + c;
@@ -131,11 +135,11 @@ __device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, in
 
 // Store a loaded tile into LDS as the four quantities to be blurred.
 template <int MODE>
-__device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ][kVIn][kVInP]) {
+__device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ][kVInY][kVInP]) {
 #pragma unroll
   for (int it = 0; it < kVIters; ++it) {
-    const int t = threadIdx.x + it * kThreads;
-    if (t < kVIn * kVIn) {
+    const int t = threadIdx.x + it * kVThreads;
+    if (t < kVInY * kVIn) {
       const int r = t / kVIn, c = t - r * kVIn;
       if constexpr (MODE == kBwd) {
 #pragma unroll
@@ -152,24 +156,24 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
   }
 }
 
-// X pass of one staged slice: 26 rows x 16 columns of partial sums, stored
+// X pass of one staged slice: 42 rows x 16 columns of partial sums, stored
 // column-major (Bx[q][column][row]).  A task is 4 adjacent outputs of one
 // quantity in one row, formed from 16 columns read as four 16-byte words;
 // consecutive lanes take consecutive rows, so with the 28-float row pitch
 // any 8 (or 16) of them read distinct bank groups, and their 4 single-word
 // stores land on consecutive words.  The Y pass then reads 11 consecutive
-// words per lane, and the 26-word column pitch spreads a half-wave's 16
+// words per lane, and the 42-word column pitch spreads a half-wave's 16
 // columns x 2 rows over 32 distinct banks.
-constexpr int kXTasks = kQ * (kVT / 4) * kVIn;
-__device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
-                                          float (&Bx)[kQ][kVT][kVIn]) {
+constexpr int kXTasks = kQ * (kVT / 4) * kVInY;
+__device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
+                                          float (&Bx)[kQ][kVT][kVInY]) {
 #pragma unroll
-  for (int it = 0; it < (kXTasks + kThreads - 1) / kThreads; ++it) {
-    const int t = threadIdx.x + it * kThreads;
+  for (int it = 0; it < (kXTasks + kVThreads - 1) / kVThreads; ++it) {
+    const int t = threadIdx.x + it * kVThreads;
     if (t < kXTasks) {
-      const int q = t / ((kVT / 4) * kVIn);
-      const int rem = t - q * ((kVT / 4) * kVIn);
-      const int g = rem / kVIn, r = rem - g * kVIn;
+      const int q = t / ((kVT / 4) * kVInY);
+      const int rem = t - q * ((kVT / 4) * kVInY);
+      const int g = rem / kVInY, r = rem - g * kVInY;
       const float* src = &A[q][r][4 * g];
       float v[16];
 #pragma unroll
@@ -195,7 +199,7 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVIn][kVInP],
 }
 
 // Y pass at this lane's (i, j) of one X-blurred slice.
-__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVIn], float (&a)[kQ]) {
+__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVInY], float (&a)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -271,9 +275,9 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
 
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
-  __shared__ __align__(16) float A[2][kQ][kVIn][kVInP];
-  __shared__ __align__(16) float Bx[2][kQ][kVT][kVIn];
-  __shared__ double red[kWaves];
+  __shared__ __align__(16) float A[2][kQ][kVInY][kVInP];
+  __shared__ __align__(16) float Bx[2][kQ][kVT][kVInY];
+  __shared__ double red[kVWaves];
   constexpr unsigned kEb = img_bytes<T>();
 
   float dl = 0.0f;
@@ -285,7 +289,7 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     const int64_t tiles = (int64_t)p.tiles_x * p.tiles_y;
     const int64_t v = sc / tiles;
     const int tt = (int)(sc - v * tiles);
-    s.i0 = (tt / p.tiles_x) * kVT;
+    s.i0 = (tt / p.tiles_x) * kVTy;
     s.j0 = (tt % p.tiles_x) * kVT;
     s.k0 = w.row_begin;
     s.nk = w.row_end - w.row_begin;
@@ -352,7 +356,7 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     q.ws = p.ws;
     q.loss = p.loss;
     q.inv_m = p.inv_m;
-    finish_loss<kWaves>(q, acc, red);
+    finish_loss<kVWaves>(q, acc, red);
   }
 }
 
