@@ -153,7 +153,11 @@ SHAPES = [((1, 1, 11, 11), "valid"), ((1, 1, 1, 1), "same"), ((1, 1, 3, 7), "sam
           ((1, 2, 67, 133), "valid"), ((2, 1, 40, 245), "same"), ((1, 1, 300, 517), "valid"),
           ((1, 3, 129, 500), "same"), ((1, 1, 16, 1000), "valid"), ((3, 1, 23, 254), "same"),
           ((1, 1, 130, 236), "valid"), ((1, 1, 81, 237), "same"), ((1, 1, 41, 472), "valid"),
-          ((300, 1, 24, 480), "valid"), ((2, 2, 260, 96), "same")]
+          ((300, 1, 24, 480), "valid"), ((2, 2, 260, 96), "same"),
+          # many planes side by side: widths around the 246-column pitch floor,
+          # odd widths (per-column stores), planes narrower than a strip
+          ((5, 2, 30, 247), "same"), ((4, 3, 20, 13), "valid"), ((7, 1, 15, 246), "valid"),
+          ((3, 3, 12, 1921), "same")]
 
 
 @pytest.mark.parametrize("path", list(RUNNERS))
