@@ -10,9 +10,10 @@
 // gradients only (and, with the loss, that is the whole training step).
 //
 // Two stencil stages run in one strip of 256 lanes:
-//   stage 1 : lane t owns image column v0 - 10 + t; the column pass of the
-//             four quantities runs through a 12-slot register ring, the row
-//             pass through the LDS tile, as in the two-kernel design.  Each
+//   stage 1 : lane t owns image column v0 - 10 + t (v0: the strip's first
+//             gradient column); the column pass of the four quantities runs
+//             through a 12-slot register ring, the row pass through the LDS
+//             tile, as in the two-kernel design.  Each
 //             row-pass lane forms the SSIM terms and the four loss partials
 //             at 4 adjacent map entries and writes the partials back into the
 //             same tile row it read (zero outside the map: the adjoint's zero
@@ -22,13 +23,17 @@
 //             through a second register ring, writes the result back into
 //             the same column, and the row pass gives 4 adjacent gradient
 //             entries per lane: 236 gradient columns per strip.
+// Strips run over the N*C planes laid side by side, each followed by a gap
+// of zero columns (Params::vpitch): a strip may end in one plane and go on
+// into the next, so planes whose width is not a multiple of 236 share their
+// last strips instead of each paying a mostly empty one.
 // Row pipeline: image row r enters stage 1; it completes map row
 // r + off - 10, whose partials complete gradient row r - 10 in stage 2.  A
 // row range of n gradient rows therefore reads n + 20 image rows, each once:
 // stage 1 also keeps the rows it loads in an LDS ring, from which stage 2
-// takes x and y for the chain rule.  Map
-// entries shared by two strips or two row ranges are computed by both, and
-// the loss counts each exactly once, in the strip and range that own it.
+// takes x and y for the chain rule.  Map entries shared by two strips or two
+// row ranges are computed by both, and the loss counts each exactly once, in
+// the strip and range that own it.
 //
 // The tile is double-buffered per batch of 4 rows; within a batch it holds,
 // in turn, the column-blurred quantities, the partials (written over the row
