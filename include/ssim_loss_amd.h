@@ -99,8 +99,9 @@ size_t ssim_saved_maps_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int pad
 /* Bytes of the workspace ssim_forward needs (the loss reduction's
  * accumulator: a fixed-point sum and a completion count in one 64-bit word).
  * The caller zero-fills it once, before its first use; every ssim_forward
- * leaves it ready for the next call (the last workgroup resets it).  One workspace must not be used by
- * two ssim_forward calls that may run at the same time.  Host-only. */
+ * leaves it ready for the next call (the last workgroup resets it).  One
+ * workspace must not be used by two ssim_forward calls that may run at the
+ * same time.  Host-only. */
 size_t ssim_workspace_bytes(void);
 
 /* Forward.  Computes loss = 1 - (1/M) * sum over the N*C*Ho*Wo map entries
@@ -122,7 +123,10 @@ size_t ssim_workspace_bytes(void);
  *                 before its first use
  *   stream      : hipStream_t (NULL = default stream)
  *
- * The reduction is deterministic: the same inputs give the same bits. */
+ * The reduction is deterministic: the same inputs give the same bits.  A NaN
+ * or infinite image value makes the loss NaN (and the workspace is still
+ * left ready for the next call); every loss-forming entry point below does
+ * the same. */
 int ssim_forward(const float* img1, const float* img2, int64_t N, int64_t C, int64_t H,
                  int64_t W, int padding, float* loss, float* saved_maps, void* workspace,
                  void* stream);
