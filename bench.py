@@ -417,6 +417,24 @@ def main():
              and (args.all_kernels or k in DESIGNS[args.design])]
     kern = {k: per_launch_ms(launches[k]) for k in timed}
 
+    # the autograd path (ssim_loss(...).backward(): inference forward, then
+    # the recomputing backward, with torch's autograd bookkeeping), timed
+    # with events around K whole steps
+    autograd = None
+    if args.all_kernels and args.dtype == "float32":
+        a1 = t1.detach().clone().requires_grad_(True)
+
+        def ag_step():
+            a1.grad = None
+            S.ssim_loss(a1, t2, w.padding).backward()
+
+        for _ in range(5):
+            ag_step()
+        torch.cuda.synchronize()
+        ag_ms = per_launch_ms(ag_step)
+        autograd = {"ms_per_step": round(ag_ms, 5), "mpix_per_s": round(mpix / (ag_ms * 1e-3), 1),
+                    "launches": "ssim_forward (inference) + ssim_backward_recompute"}
+
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
     if args.cold_steps > 0:
@@ -528,6 +546,7 @@ def main():
         }),
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "designs": designs,
+        "autograd": autograd,
         "cold": cold,
         "rates": {
             "melem_per_s": round(N * C * H * W * K / elapsed / 1e6, 1),
