@@ -11,11 +11,13 @@
 // One workgroup (512 lanes) owns a 32 x 16 tile of output (i, j) positions of
 // one volume and marches along depth.  Each input slice is staged as a
 // 42 x 26 tile in LDS (loaded one step ahead into registers), blurred in X
-// (42 x 16 partial sums, through LDS) and in Y (32 x 16), and each lane
-// feeds its four XY-blurred values to 11 running sums per quantity that form
-// the Z pass (each sum moves one tap per slice inside its multiply-add, so
-// the register indices stay fixed without unrolling the depth loop).  The
-// three LDS stages of consecutive slices are software-pipelined over
+// (42 x 16 partial sums, through LDS) and in Y (32 x 16: each lane forms 4
+// outputs of one quantity down one column, and writes them to a transpose
+// tile), and each lane then takes the four XY-blurred quantities at its own
+// position and feeds them to 11 running sums per quantity that form the Z
+// pass (each sum moves one tap per slice inside its multiply-add, so the
+// register indices stay fixed without unrolling the depth loop).  The four
+// LDS stages of consecutive slices are software-pipelined over
 // double-buffered tiles, one barrier per slice.
 //
 // Training forward: the loss partials m0..m3 (ssim_device.hpp) are saved at
@@ -34,12 +36,17 @@ constexpr int kVTy = 32;          // output tile rows (i)
 constexpr int kVIn = kVT + 10;    // input tile columns
 constexpr int kVInY = kVTy + 10;  // input tile rows
 constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
+constexpr int kVByP = (kVInY + 3) / 4 * 4;  // column pitch of the X-blurred tile (16-byte columns)
+constexpr int kVCP = kVT + 1;     // row pitch of the Y pass's transpose tile
 constexpr int kVThreads = kVT * kVTy;    // one output position per lane
 constexpr int kVWaves = kVThreads / kWave;
 constexpr int kVMinSlices = 16;   // shortest depth range of one workgroup
 static_assert(kVThreads % kWave == 0, "whole waves");
 static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
               "X-pass tasks read whole 16-byte words inside a tile row");
+static_assert(kQ * kVT * (kVTy / 4) == kVThreads, "one Y-pass task (4 outputs) per lane");
+static_assert(kVByP % 4 == 0 && 4 * (kVTy / 4 - 1) + 14 <= kVInY,
+              "Y-pass tasks read 16-byte words of rows the X pass wrote");
 
 struct VolParams {
   int D, H, W;          // volume extent
@@ -157,16 +164,14 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
 }
 
 // X pass of one staged slice: 42 rows x 16 columns of partial sums, stored
-// column-major (Bx[q][column][row]).  A task is 4 adjacent outputs of one
-// quantity in one row, formed from 16 columns read as four 16-byte words;
-// consecutive lanes take consecutive rows, so with the 28-float row pitch
-// any 8 (or 16) of them read distinct bank groups, and their 4 single-word
-// stores land on consecutive words.  The Y pass then reads 11 consecutive
-// words per lane, and the 42-word column pitch spreads a half-wave's 16
-// columns x 2 rows over 32 distinct banks.
+// column-major (Bx[q][column][row], columns padded to 44 words).  A task is
+// 4 adjacent outputs of one quantity in one row, formed from 16 columns read
+// as four 16-byte words; consecutive lanes take consecutive rows, so with
+// the 28-float row pitch any 8 (or 16) of them read distinct bank groups,
+// and their 4 single-word stores land on consecutive words.
 constexpr int kXTasks = kQ * (kVT / 4) * kVInY;
 __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
-                                          float (&Bx)[kQ][kVT][kVInY]) {
+                                          float (&Bx)[kQ][kVT][kVByP]) {
 #pragma unroll
   for (int it = 0; it < (kXTasks + kVThreads - 1) / kVThreads; ++it) {
     const int t = threadIdx.x + it * kVThreads;
@@ -198,16 +203,45 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
   }
 }
 
-// Y pass at this lane's (i, j) of one X-blurred slice.
-__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVInY], float (&a)[kQ]) {
+// Y pass of one X-blurred slice.  A task (one per lane) is 4 outputs of one
+// quantity down one column, rows 4g .. 4g + 3, from the 14 words of that
+// column starting at row 4g, read as three 16-byte words and one 8-byte
+// word: 3.5 words per output instead of 11.  Consecutive lanes take
+// consecutive g, so any 8 of them read 128 contiguous bytes.  The outputs go
+// to the transpose tile C[q][row][column], whose 17-word row pitch puts a
+// half-wave's 8 g x 4 columns on 32 distinct banks.
+__device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
+                                          float (&C)[kQ][kVTy][kVCP]) {
+  const int t = threadIdx.x;
+  const int g = t % (kVTy / 4), tx = (t / (kVTy / 4)) % kVT, q = t / ((kVTy / 4) * kVT);
+  const float* src = &Bx[q][tx][4 * g];
+  float v[14];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+    v[4 * k + 0] = f.x;
+    v[4 * k + 1] = f.y;
+    v[4 * k + 2] = f.z;
+    v[4 * k + 3] = f.w;
+  }
+  const float2 f2 = *reinterpret_cast<const float2*>(src + 12);
+  v[12] = f2.x;
+  v[13] = f2.y;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float a = tap(0) * v[u];
+#pragma unroll
+    for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
+    C[q][4 * g + u][tx] = a;
+  }
+}
+
+// The four XY-blurred quantities at this lane's (i, j), from the transpose
+// tile the Y pass wrote.
+__device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVTy][kVCP], float (&a)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    float s = tap(0) * Bx[q][tx][ty];
-#pragma unroll
-    for (int b = 1; b < 11; ++b) s = __builtin_fmaf(tap(b), Bx[q][tx][ty + b], s);
-    a[q] = s;
-  }
+  for (int q = 0; q < kQ; ++q) a[q] = C[q][ty][tx];
 }
 
 // Z pass as running sums: acc[c] holds the partial sum, over the slices seen
@@ -276,7 +310,8 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
   __shared__ __align__(16) float A[2][kQ][kVInY][kVInP];
-  __shared__ __align__(16) float Bx[2][kQ][kVT][kVInY];
+  __shared__ __align__(16) float Bx[2][kQ][kVT][kVByP];
+  __shared__ float C[2][kQ][kVTy][kVCP];
   __shared__ double red[kVWaves];
   constexpr unsigned kEb = img_bytes<T>();
 
@@ -314,11 +349,12 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
 
     // Input slices kin0 .. kin0 + nsl - 1 pass through the lane's running
     // sums; the first 10 only start them, and slice kin0 + 10 + n completes
-    // output slice k0 + n.  Three stages per slice, one step apart, each
+    // output slice k0 + n.  Four stages per slice, one step apart, each
     // step ending in the only barrier: in step j the tile of slice j goes
     // into A[j & 1] (its loads were issued in step j - 1), slice j - 1 is
-    // blurred in X from A[(j - 1) & 1] into Bx[(j - 1) & 1], and slice j - 2
-    // in Y from Bx[j & 1], then in Z.  No buffer is written in the step that
+    // blurred in X from A[(j - 1) & 1] into Bx[(j - 1) & 1], slice j - 2 in
+    // Y from Bx[j & 1] into C[j & 1], and slice j - 3 is taken from
+    // C[(j - 1) & 1] into the Z sums.  No buffer is written in the step that
     // reads its other use, and each stage reads what an earlier step wrote.
     float acc_z[11][kQ];
 #pragma unroll
@@ -330,22 +366,23 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     VolPre<MODE> pre;
     vol_load<MODE, T>(p, s, kin0, pre);
     float xy[2] = {0.0f, 0.0f};
-    for (int j = 0; j < nsl + 2; ++j) {
+    for (int j = 0; j < nsl + 3; ++j) {
       if (j < nsl) {
         vol_store<MODE>(pre, A[j & 1]);
         vol_load<MODE, T>(p, s, kin0 + j + 1, pre);
       }
       if (j >= 1 && j <= nsl) vol_xpass(A[(j - 1) & 1], Bx[(j - 1) & 1]);
-      // (before slice 0 reaches the Y pass the sums take zeros, which leave
+      if (j >= 2 && j <= nsl + 1) vol_ypass(Bx[j & 1], C[j & 1]);
+      // (before slice 0 reaches the Z pass the sums take zeros, which leave
       // them unchanged but keep their update out of any branch)
       float a[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (j >= 2) vol_ypass(Bx[j & 1], a);
+      if (j >= 3) vol_ytake(C[(j - 1) & 1], a);
       vol_zpass(acc_z, a);
-      const int n = j - 12;  // output slice k0 + n, once its 11 slices are in
+      const int n = j - 13;  // output slice k0 + n, once its 11 slices are in
       if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, acc_z[10], xy, dl, acc);
       // the chain rule's x, y for the next step's output slice
       if constexpr (MODE == kBwd) {
-        if (j >= 11 && j < nsl + 1) vol_load_xy<T>(p, s, s.k0 + j - 11, xy);
+        if (j >= 12 && j < nsl + 2) vol_load_xy<T>(p, s, s.k0 + j - 12, xy);
       }
       __syncthreads();
     }
