@@ -247,17 +247,52 @@ __device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVTy][kVCP], floa
 // Z pass as running sums: acc[c] holds the partial sum, over the slices seen
 // so far, of the output whose window has the newest slice at tap c.  Each new
 // XY-blurred value a moves every sum one tap on, acc[c] <- acc[c - 1] +
-// g[c] a (the multiply-add writes the moved sum, so no register is copied),
-// and acc[10] is then the complete sum, in tap order, of the output whose
-// window ends at the new slice.
+// g[c] a, and acc[10] is then the complete sum, in tap order, of the output
+// whose window ends at the new slice.
+//
+// Each move is one v_fmamk_f32 (d = s0 * literal + s1, fused, with its own
+// destination), taken in descending c so that acc[c] is overwritten only
+// after acc[c + 1] has read it: the sums then stay in their registers across
+// the depth loop.  Written with the accumulate form (d += s0 * literal) the
+// compiler computed each new sum in its predecessor's register and rotated
+// all 40 back with register copies on every slice.  The literals are the fp32
+// bits of the taps, checked against them below.
+#define SSIM_TAP0_BITS 0x3a86cab6
+#define SSIM_TAP1_BITS 0x3bf8ff01
+#define SSIM_TAP2_BITS 0x3d13758c
+#define SSIM_TAP3_BITS 0x3ddff87f
+#define SSIM_TAP4_BITS 0x3e5a1e20
+#define SSIM_TAP5_BITS 0x3e8832b0
+static_assert(__builtin_bit_cast(unsigned, kTap0) == SSIM_TAP0_BITS &&
+                  __builtin_bit_cast(unsigned, kTap1) == SSIM_TAP1_BITS &&
+                  __builtin_bit_cast(unsigned, kTap2) == SSIM_TAP2_BITS &&
+                  __builtin_bit_cast(unsigned, kTap3) == SSIM_TAP3_BITS &&
+                  __builtin_bit_cast(unsigned, kTap4) == SSIM_TAP4_BITS &&
+                  __builtin_bit_cast(unsigned, kTap5) == SSIM_TAP5_BITS,
+              "the Z pass's literals are the taps' fp32 bits");
+#define SSIM_STR_(x) #x
+#define SSIM_STR(x) SSIM_STR_(x)
+#define SSIM_ZMOVE(c, BITS)                                                  \
+  asm("v_fmamk_f32 %0, %1, " SSIM_STR(BITS) ", %2"                           \
+      : "=v"(acc[c][q])                                                      \
+      : "v"(a[q]), "v"(acc[c - 1][q]))
 __device__ __forceinline__ void vol_zpass(float (&acc)[11][kQ], const float (&a)[kQ]) {
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-#pragma unroll
-    for (int c = 10; c > 0; --c) acc[c][q] = __builtin_fmaf(tap(c), a[q], acc[c - 1][q]);
+    SSIM_ZMOVE(10, SSIM_TAP0_BITS);  // tap 10 = tap 0
+    SSIM_ZMOVE(9, SSIM_TAP1_BITS);
+    SSIM_ZMOVE(8, SSIM_TAP2_BITS);
+    SSIM_ZMOVE(7, SSIM_TAP3_BITS);
+    SSIM_ZMOVE(6, SSIM_TAP4_BITS);
+    SSIM_ZMOVE(5, SSIM_TAP5_BITS);
+    SSIM_ZMOVE(4, SSIM_TAP4_BITS);
+    SSIM_ZMOVE(3, SSIM_TAP3_BITS);
+    SSIM_ZMOVE(2, SSIM_TAP2_BITS);
+    SSIM_ZMOVE(1, SSIM_TAP1_BITS);
     acc[0][q] = tap(0) * a[q];
   }
 }
+#undef SSIM_ZMOVE
 
 // Where output slice k at this lane's (i, j) lives: its element offset in
 // bytes for elements of eb bytes, or kOob outside the output extent.
