@@ -37,7 +37,6 @@ constexpr int kVIn = kVT + 10;    // input tile columns
 constexpr int kVInY = kVTy + 10;  // input tile rows
 constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
 constexpr int kVByP = (kVInY + 3) / 4 * 4;  // column pitch of the X-blurred tile (16-byte columns)
-constexpr int kVCP = kVT + 1;     // row pitch of the Y pass's transpose tile
 constexpr int kVThreads = kVT * kVTy;    // one output position per lane
 constexpr int kVWaves = kVThreads / kWave;
 constexpr int kVMinSlices = 16;   // shortest depth range of one workgroup
@@ -45,8 +44,10 @@ static_assert(kVThreads % kWave == 0, "whole waves");
 static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
               "X-pass tasks read whole 16-byte words inside a tile row");
 static_assert(kQ * kVT * (kVTy / 4) == kVThreads, "one Y-pass task (4 outputs) per lane");
-static_assert(kVByP % 4 == 0 && 4 * (kVTy / 4 - 1) + 14 <= kVInY,
-              "Y-pass tasks read 16-byte words of rows the X pass wrote");
+static_assert(kVByP % 4 == 0 && 4 * (kVTy / 4 - 1) + 14 <= kVInY &&
+                  4 * (kVTy / 4 - 1) + 16 <= kVByP,
+              "Y-pass tasks read 16-byte words inside a column, of rows the X pass wrote");
+static_assert(kVT == 16 && kVTy % 8 == 0, "the transpose tile's bank layout assumes 16 columns");
 
 struct VolParams {
   int D, H, W;          // volume extent
@@ -203,45 +204,47 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
   }
 }
 
+// Row r of the transpose tile is stored at row r ^ bit 2 of r (rows 4..7,
+// 12..15, ... swap in pairs), so that with its 16-word rows both the Y pass's
+// stores (16 columns x rows 4g + u and 4g + 4 + u per half-wave) and the Z
+// pass's loads (16 columns x rows 2k and 2k + 1) fall on 32 distinct banks.
+__device__ __forceinline__ int vol_crow(int r) { return r ^ ((r >> 2) & 1); }
+
 // Y pass of one X-blurred slice.  A task (one per lane) is 4 outputs of one
 // quantity down one column, rows 4g .. 4g + 3, from the 14 words of that
-// column starting at row 4g, read as three 16-byte words and one 8-byte
-// word: 3.5 words per output instead of 11.  Consecutive lanes take
-// consecutive g, so any 8 of them read 128 contiguous bytes.  The outputs go
-// to the transpose tile C[q][row][column], whose 17-word row pitch puts a
-// half-wave's 8 g x 4 columns on 32 distinct banks.
+// column starting at row 4g, read as four 16-byte words (the last two words
+// unused): 4 reads per 4 outputs instead of 44.  Consecutive lanes take
+// consecutive columns, whose 44-word pitch puts any 8 of them on distinct
+// bank quads.  The outputs go to the transpose tile C[q][row][column].
 __device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
-                                          float (&C)[kQ][kVTy][kVCP]) {
+                                          float (&C)[kQ][kVTy][kVT]) {
   const int t = threadIdx.x;
-  const int g = t % (kVTy / 4), tx = (t / (kVTy / 4)) % kVT, q = t / ((kVTy / 4) * kVT);
+  const int tx = t % kVT, g = (t / kVT) % (kVTy / 4), q = t / (kVT * (kVTy / 4));
   const float* src = &Bx[q][tx][4 * g];
-  float v[14];
+  float v[16];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < 4; ++k) {
     const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
     v[4 * k + 0] = f.x;
     v[4 * k + 1] = f.y;
     v[4 * k + 2] = f.z;
     v[4 * k + 3] = f.w;
   }
-  const float2 f2 = *reinterpret_cast<const float2*>(src + 12);
-  v[12] = f2.x;
-  v[13] = f2.y;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float a = tap(0) * v[u];
 #pragma unroll
     for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
-    C[q][4 * g + u][tx] = a;
+    C[q][vol_crow(4 * g + u)][tx] = a;
   }
 }
 
 // The four XY-blurred quantities at this lane's (i, j), from the transpose
 // tile the Y pass wrote.
-__device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVTy][kVCP], float (&a)[kQ]) {
+__device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVTy][kVT], float (&a)[kQ]) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) a[q] = C[q][ty][tx];
+  for (int q = 0; q < kQ; ++q) a[q] = C[q][vol_crow(ty)][tx];
 }
 
 // Z pass as running sums: acc[c] holds the partial sum, over the slices seen
@@ -346,7 +349,7 @@ template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
   __shared__ __align__(16) float A[2][kQ][kVInY][kVInP];
   __shared__ __align__(16) float Bx[2][kQ][kVT][kVByP];
-  __shared__ float C[2][kQ][kVTy][kVCP];
+  __shared__ float C[2][kQ][kVTy][kVT];
   __shared__ double red[kVWaves];
   constexpr unsigned kEb = img_bytes<T>();
 
