@@ -296,6 +296,14 @@ __device__ __forceinline__ void vol_zpass(float (&acc)[11][kQ], const float (&a)
   }
 }
 #undef SSIM_ZMOVE
+#undef SSIM_STR
+#undef SSIM_STR_
+#undef SSIM_TAP0_BITS
+#undef SSIM_TAP1_BITS
+#undef SSIM_TAP2_BITS
+#undef SSIM_TAP3_BITS
+#undef SSIM_TAP4_BITS
+#undef SSIM_TAP5_BITS
 
 // Where output slice k at this lane's (i, j) lives: its element offset in
 // bytes for elements of eb bytes, or kOob outside the output extent.
