@@ -1,7 +1,10 @@
 // ssim_api.hip -- host side of the fused SSIM loss: the C ABI declared in
 // ssim_loss_amd.h, argument checks (all before any HIP call), per-device
-// launch planning and the launches.  The kernels live in ssim_device.hpp and
-// are instantiated per image type in ssim_kernels_{f32,f16,bf16}.hip.
+// launch planning and the launches.  The kernels live in ssim_device.hpp
+// (the saved-maps strip kernels and the shared arithmetic), ssim_fused.hpp
+// (the recomputing kernels) and ssim_vol.hpp (volumes); ssim_entry.hpp
+// declares the entry kernels, instantiated per image type in
+// ssim_kernels_{f32,f16,bf16}.hip.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
