@@ -109,16 +109,10 @@ struct VolPre {
   float v[kVIters][MODE == kBwd ? 4 : 2];
 };
 
-// Issue the loads of input slice kin's tile (rows i0 - off .., columns
-// j0 - off ..).  Outside the blurred input's extent a load reads 0 (an
-// out-of-range offset): for the forward x = y = 0, for the backward a zero
-// partial.  Every lane runs every iteration; positions past the tile use an
-// out-of-range offset too.
-template <int MODE, int T>
-__device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, int kin,
-                                         VolPre<MODE>& pre) {
-  constexpr unsigned kEb = img_bytes<T>();
-  const bool kok = (unsigned)kin < (unsigned)p.in_d;
+// This lane's staged-tile positions as element offsets within one input
+// slice (kOob outside the tile or the slice), once per segment.
+__device__ __forceinline__ void vol_tile_offsets(const VolParams& p, const VolSeg& s,
+                                                 unsigned (&eo)[kVIters]) {
 #pragma unroll
   for (int it = 0; it < kVIters; ++it) {
     const int t = threadIdx.x + it * kVThreads;
@@ -126,15 +120,29 @@ __device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, in
     const int tt = in_tile ? t : 0;
     const int r = tt / kVIn, c = tt - r * kVIn;
     const int ii = s.i0 - p.off + r, jj = s.j0 - p.off + c;
-    const bool ok = in_tile && kok && (unsigned)ii < (unsigned)p.in_h &&
-                    (unsigned)jj < (unsigned)p.in_w;
-    const unsigned e = ok ? (unsigned)(((int64_t)kin * p.in_h + ii) * p.in_w + jj) : 0u;
+    const bool ok = in_tile && (unsigned)ii < (unsigned)p.in_h && (unsigned)jj < (unsigned)p.in_w;
+    eo[it] = ok ? (unsigned)(ii * p.in_w + jj) : kOob;
+  }
+}
+
+// Issue the loads of input slice kin's tile.  Outside the blurred input's
+// extent a load reads 0 (an out-of-range offset): for the forward x = y = 0,
+// for the backward a zero partial.
+template <int MODE, int T>
+__device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, int kin,
+                                         const unsigned (&eo)[kVIters], VolPre<MODE>& pre) {
+  constexpr unsigned kEb = img_bytes<T>();
+  const bool kok = (unsigned)kin < (unsigned)p.in_d;
+  const unsigned slice = kok ? (unsigned)kin * (unsigned)(p.in_h * p.in_w) : 0u;
+#pragma unroll
+  for (int it = 0; it < kVIters; ++it) {
+    const bool ok = kok && eo[it] != kOob;
     if constexpr (MODE == kBwd) {
-      const unsigned off = ok ? e * 4u : kOob;
+      const unsigned off = ok ? (slice + eo[it]) * 4u : kOob;
 #pragma unroll
       for (int q = 0; q < kQ; ++q) pre.v[it][q] = ld1(s.in[q], off);
     } else {
-      const unsigned off = ok ? e * kEb : kOob;
+      const unsigned off = ok ? (slice + eo[it]) * kEb : kOob;
       pre.v[it][0] = ld_img<T>(s.in[0], off);
       pre.v[it][1] = ld_img<T>(s.in[1], off);
     }
@@ -305,22 +313,28 @@ __device__ __forceinline__ void vol_zpass(float (&acc)[11][kQ], const float (&a)
 #undef SSIM_TAP4_BITS
 #undef SSIM_TAP5_BITS
 
-// Where output slice k at this lane's (i, j) lives: its element offset in
-// bytes for elements of eb bytes, or kOob outside the output extent.
-__device__ __forceinline__ unsigned vol_out_off(const VolParams& p, const VolSeg& s, int k,
-                                                unsigned eb) {
+// This lane's (i, j) as an element offset within one output slice, or kOob
+// outside the output extent (once per segment).
+__device__ __forceinline__ unsigned vol_out_pos(const VolParams& p, const VolSeg& s) {
   const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
   const int i = s.i0 + ty, j = s.j0 + tx;
-  const bool ok = (unsigned)k < (unsigned)p.out_d && i < p.out_h && j < p.out_w;
-  return ok ? (unsigned)(((int64_t)k * p.out_h + i) * p.out_w + j) * eb : kOob;
+  return (i < p.out_h && j < p.out_w) ? (unsigned)(i * p.out_w + j) : kOob;
+}
+
+// Where output slice k at this lane's (i, j) lives: its byte offset for
+// elements of eb bytes, or kOob outside the output extent.
+__device__ __forceinline__ unsigned vol_out_off(const VolParams& p, int k, unsigned oo,
+                                                unsigned eb) {
+  const bool ok = (unsigned)k < (unsigned)p.out_d && oo != kOob;
+  return ok ? ((unsigned)k * (unsigned)(p.out_h * p.out_w) + oo) * eb : kOob;
 }
 
 // Backward: x and y at output slice k of this lane (issued a step before the
 // chain rule needs them).
 template <int T>
 __device__ __forceinline__ void vol_load_xy(const VolParams& p, const VolSeg& s, int k,
-                                            float (&xy)[2]) {
-  const unsigned off = vol_out_off(p, s, k, img_bytes<T>());
+                                            unsigned oo, float (&xy)[2]) {
+  const unsigned off = vol_out_off(p, k, oo, img_bytes<T>());
   xy[0] = ld_img<T>(s.img[0], off);
   xy[1] = ld_img<T>(s.img[1], off);
 }
@@ -330,10 +344,10 @@ __device__ __forceinline__ void vol_load_xy(const VolParams& p, const VolSeg& s,
 // chain rule with this voxel's x, y (xy) and both gradients.
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s, int k,
-                                            const float (&o)[kQ], const float (&xy)[2], float dl,
-                                            double& acc) {
+                                            unsigned oo, const float (&o)[kQ],
+                                            const float (&xy)[2], float dl, double& acc) {
   if constexpr (MODE == kBwd) {
-    const unsigned off = vol_out_off(p, s, k, img_bytes<T>());
+    const unsigned off = vol_out_off(p, k, oo, img_bytes<T>());
     const float xv = xy[0], yv = xy[1];
     const float xs = xv - kShift, ys = yv - kShift, d = xv - yv;
     const float g1 = dl * __builtin_fmaf(d, o[2], __builtin_fmaf(ys, o[3], o[0]));
@@ -341,7 +355,7 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
     st_img<T, kNt>(s.out[0], off, g1);
     st_img<T, kNt>(s.out[1], off, g2);
   } else {
-    const unsigned off = vol_out_off(p, s, k, 4u);
+    const unsigned off = vol_out_off(p, k, oo, 4u);
     const SsimTerms st = ssim_terms(o[0], o[1], o[2], o[3]);
     acc += off != kOob ? (double)one_minus_ssim(st) : 0.0;
     if constexpr (MODE == kFwdTrain) {
@@ -409,13 +423,16 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       for (int q = 0; q < kQ; ++q) acc_z[k][q] = 0.0f;
     const int kin0 = s.k0 - p.off;
     const int nsl = 10 + s.nk;
+    unsigned eo[kVIters];
+    vol_tile_offsets(p, s, eo);
+    const unsigned oo = vol_out_pos(p, s);
     VolPre<MODE> pre;
-    vol_load<MODE, T>(p, s, kin0, pre);
+    vol_load<MODE, T>(p, s, kin0, eo, pre);
     float xy[2] = {0.0f, 0.0f};
     for (int j = 0; j < nsl + 3; ++j) {
       if (j < nsl) {
         vol_store<MODE>(pre, A[j & 1]);
-        vol_load<MODE, T>(p, s, kin0 + j + 1, pre);
+        vol_load<MODE, T>(p, s, kin0 + j + 1, eo, pre);
       }
       if (j >= 1 && j <= nsl) vol_xpass(A[(j - 1) & 1], Bx[(j - 1) & 1]);
       if (j >= 2 && j <= nsl + 1) vol_ypass(Bx[j & 1], C[j & 1]);
@@ -425,10 +442,10 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       if (j >= 3) vol_ytake(C[(j - 1) & 1], a);
       vol_zpass(acc_z, a);
       const int n = j - 13;  // output slice k0 + n, once its 11 slices are in
-      if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, acc_z[10], xy, dl, acc);
+      if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, oo, acc_z[10], xy, dl, acc);
       // the chain rule's x, y for the next step's output slice
       if constexpr (MODE == kBwd) {
-        if (j >= 12 && j < nsl + 2) vol_load_xy<T>(p, s, s.k0 + j - 12, xy);
+        if (j >= 12 && j < nsl + 2) vol_load_xy<T>(p, s, s.k0 + j - 12, oo, xy);
       }
       __syncthreads();
     }
