@@ -41,11 +41,13 @@ def vol_run(x, y, padding, dloss=1.0, dtype="float32", grad1=True, grad2=True, t
     return lv, f(g1), f(g2)
 
 
-# around the window (11), the 16 x 16 tile, the 24-slice depth ranges, and
-# volumes smaller than the window (same)
+# around the window (11), the 32 x 16 (rows x columns) output tile, several
+# depth ranges per tile-column, and volumes smaller than the window (same)
 SHAPES = [((1, 1, 11, 11, 11), "valid"), ((1, 1, 1, 1, 1), "same"), ((1, 1, 3, 5, 7), "same"),
           ((1, 2, 20, 17, 33), "valid"), ((2, 1, 13, 16, 16), "same"), ((1, 1, 50, 12, 40), "same"),
-          ((1, 3, 26, 27, 15), "valid"), ((3, 2, 9, 31, 18), "same")]
+          ((1, 3, 26, 27, 15), "valid"), ((3, 2, 9, 31, 18), "same"),
+          ((1, 1, 40, 70, 35), "same"), ((1, 2, 33, 34, 17), "same"), ((2, 1, 30, 43, 40), "valid"),
+          ((1, 1, 24, 100, 200), "same")]
 
 
 # The kernels blur x - 1/2 and y - 1/2, so a blurred mean is held as
