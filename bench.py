@@ -306,13 +306,15 @@ def bench_volume(args, w, x, y):
         "data": "synthetic",
         "config": {"workload": args.workload, "shape": list(x.shape), "padding": w.padding,
                    "design": "saved partials"},
-        "roofline": {"kernel": dom,
-                     "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": by[dom]},
+        # the volume kernels are bound by neither roofline (LDS and latency);
+        # the nearer of the two is HBM, and the ALU position goes beside it
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args, dom), "algorithmic_bytes": by[dom],
                      "alu": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
-                             "algorithmic_flops": fl[dom]},
-                     "traffic": measured_traffic(args, dom)},
+                             "algorithmic_flops": fl[dom]}},
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "loss": float(loss.item()),
         "cpu_baseline": None,
