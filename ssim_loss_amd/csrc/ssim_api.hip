@@ -266,9 +266,12 @@ int backward_impl(const float* dloss, const void* img1, const void* img2, int dt
 
 // The recomputing kernels read only the images: the backward without saved
 // maps (loss == NULL) and the one-pass loss and gradients (loss != NULL).
-// A run of n gradient rows of one strip-column reads n + 20 image rows, so
-// each workgroup gets at least kRecompMinRows rows.
-constexpr int kRecompMinRows = 40;
+// A share of n gradient rows of one strip-column takes about n/4 + 4 ticks
+// and reads n + 20 image rows.  When the work cannot fill the resident grid,
+// shorter shares on more workgroups still finish sooner, down to about
+// kRecompRowsPerBlock rows each; at least one workgroup per CU runs while
+// there are rows for it.
+constexpr int kRecompRowsPerBlock = 8;
 
 // ref (optional, with loss): the cached statistics of img2 written by
 // ssim_reference_stats; then only grad_img1 is formed.
@@ -349,12 +352,14 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
     p.map_plane = s.Ho * s.pitch;
   }
   // one resident wave of workgroups, each with an equal run of (strip-column,
-  // row) pairs, and at least kRecompMinRows rows each
+  // row) pairs; fewer when the rows are few (see kRecompRowsPerBlock)
   const int64_t rows = p.cols * (int64_t)p.out_h;
   int64_t G = (int64_t)d->cus * d->occ[dtype][which];
   if (G > kMaxBlocks) G = kMaxBlocks;
-  const int64_t by_rows = (rows + kRecompMinRows - 1) / kRecompMinRows;
-  if (G > by_rows) G = by_rows;
+  int64_t want = (rows + kRecompRowsPerBlock - 1) / kRecompRowsPerBlock;
+  if (want < d->cus) want = d->cus;
+  if (G > want) G = want;
+  if (G > rows) G = rows;
   if (G < 1) G = 1;
   void* args[] = {&p};
   if (hipLaunchKernel(kernel_table(dtype)[which], dim3((unsigned)G), dim3(kind_threads(which)), args,
