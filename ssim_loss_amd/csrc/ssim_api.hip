@@ -400,8 +400,14 @@ int check_shape3(int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int padd
 }
 
 // One resident wave of workgroups over (tile-column, output slice) work: a
-// depth range of at least kVMinSlices slices of one tile-column each, or
-// whole tile-columns.
+// depth range of one tile-column each, or whole tile-columns.  A depth range
+// pays 13 steps before its first output, so ranges are long (at least
+// kVMinSlices) while that fills the resident grid; with few tile-columns
+// they are shortened, down to kVMinSlicesIdle, until every CU has a
+// workgroup: the steps of one range are the latency, and idle CUs cost
+// nothing.
+constexpr int kVMinSlicesIdle = 4;
+
 int launch_vol(const DeviceInfo* d, int dtype, int which, VolParams& p, void* stream) {
   p.tiles_x = (p.out_w + kVT - 1) / kVT;
   p.tiles_y = (p.out_h + kVTy - 1) / kVTy;
@@ -417,6 +423,10 @@ int launch_vol(const DeviceInfo* d, int dtype, int which, VolParams& p, void* st
     int64_t parts = resident / p.cols;
     const int64_t max_parts = (p.out_d + kVMinSlices - 1) / kVMinSlices;
     if (parts > max_parts) parts = max_parts;
+    int64_t idle = d->cus / p.cols;  // one workgroup per CU
+    const int64_t max_idle = (p.out_d + kVMinSlicesIdle - 1) / kVMinSlicesIdle;
+    if (idle > max_idle) idle = max_idle;
+    if (parts < idle) parts = idle;
     if (parts < 1) parts = 1;
     p.parts = (int)parts;
     p.per_block = 1;
