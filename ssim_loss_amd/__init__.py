@@ -195,6 +195,40 @@ def _check_image(t, name, ndim=4):
         raise ValueError(f"{name} must be contiguous {layout}")
 
 
+def _check_buffer(t, name, dev, nbytes=0, dtype=None):
+    """A caller's output or state buffer: a contiguous tensor on the images'
+    device `dev` holding at least `nbytes` bytes (of `dtype`, when given).
+    None is passed on as NULL: the C function decides whether it may be."""
+    if t is None:
+        return
+    if not isinstance(t, _torch().Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise TypeError(f"{name} must be a tensor on {dev}, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.nbytes < nbytes:
+        raise ValueError(f"{name} holds {t.nbytes} bytes, needs {nbytes}")
+
+
+def _check_scalars(dev, **bufs):
+    """loss / dloss: one fp32 value each on the images' device."""
+    for name, t in bufs.items():
+        _check_buffer(t, name, dev, 4, _torch().float32)
+
+
+def _check_workspace(ws, dev):
+    global _ws_bytes
+    if _ws_bytes is None:
+        _ws_bytes = ssim_workspace_bytes()
+    _check_buffer(ws, "workspace", dev, _ws_bytes)
+
+
+_ws_bytes = None
+
+
 def ssim_forward(img1, img2, padding, loss, saved_maps, workspace) -> None:
     """Calls the C ``ssim_forward`` on torch's current stream.  All arguments
     are preallocated device tensors (saved_maps may be None)."""
@@ -205,6 +239,10 @@ def ssim_forward(img1, img2, padding, loss, saved_maps, workspace) -> None:
     if img1.dtype != img2.dtype:
         raise TypeError("img1 and img2 must have the same dtype")
     N, C, H, W = img1.shape
+    _check_scalars(img1.device, loss=loss)
+    _check_buffer(saved_maps, "saved_maps", img1.device,
+                  ssim_saved_maps_bytes(N, C, H, W, padding), _f32())
+    _check_workspace(workspace, img1.device)
     code = _dtype_code(img1)
     if code == 0:
         rc = lib().ssim_forward(_dptr(img1), _dptr(img2), N, C, H, W, _pad(padding), _dptr(loss),
@@ -223,10 +261,13 @@ def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) 
     _check_image(img2, "img2")
     if img1.dtype != img2.dtype:
         raise TypeError("img1 and img2 must have the same dtype")
-    for g in (grad_img1, grad_img2):
-        if g is not None and (g.dtype != img1.dtype or g.shape != img1.shape):
-            raise TypeError("gradients must have the images' dtype and shape")
+    if img1.shape != img2.shape:
+        raise ValueError("img1 and img2 must have the same shape")
+    _check_grads(img1, (grad_img1, grad_img2))
     N, C, H, W = img1.shape
+    _check_scalars(img1.device, dloss=dloss)
+    _check_buffer(saved_maps, "saved_maps", img1.device,
+                  ssim_saved_maps_bytes(N, C, H, W, padding), _f32())
     code = _dtype_code(img1)
     if code == 0:
         rc = lib().ssim_backward(_dptr(dloss), _dptr(img1), _dptr(img2), N, C, H, W,
@@ -240,6 +281,24 @@ def ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2) 
         raise SsimError(rc, "ssim_backward")
 
 
+def _torch():
+    import torch
+
+    return torch
+
+
+def _f32():
+    return _torch().float32
+
+
+def _check_grads(img1, grads):
+    for g in grads:
+        if g is not None:
+            if g.dtype != img1.dtype or g.shape != img1.shape:
+                raise TypeError("gradients must have the images' dtype and shape")
+            _check_buffer(g, "gradient", img1.device)
+
+
 def _check_pair_and_grads(img1, img2, grads, ndim=4):
     _check_image(img1, "img1", ndim)
     _check_image(img2, "img2", ndim)
@@ -247,15 +306,14 @@ def _check_pair_and_grads(img1, img2, grads, ndim=4):
         raise ValueError("img1 and img2 must have the same shape")
     if img1.dtype != img2.dtype:
         raise TypeError("img1 and img2 must have the same dtype")
-    for g in grads:
-        if g is not None and (g.dtype != img1.dtype or g.shape != img1.shape):
-            raise TypeError("gradients must have the images' dtype and shape")
+    _check_grads(img1, grads)
 
 
 def ssim_backward_recompute(dloss, img1, img2, padding, grad_img1, grad_img2) -> None:
     """Calls the C ``ssim_backward_recompute`` (no saved maps) on torch's
     current stream."""
     _check_pair_and_grads(img1, img2, (grad_img1, grad_img2))
+    _check_scalars(img1.device, dloss=dloss)
     N, C, H, W = img1.shape
     rc = lib().ssim_backward_recompute(_dptr(dloss), _dptr(img1), _dptr(img2), _dtype_code(img1),
                                        N, C, H, W, _pad(padding), _dptr(grad_img1),
@@ -268,6 +326,8 @@ def ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, g
     """Calls the C ``ssim_loss_and_grad`` (loss and gradients in one launch)
     on torch's current stream."""
     _check_pair_and_grads(img1, img2, (grad_img1, grad_img2))
+    _check_scalars(img1.device, dloss=dloss, loss=loss)
+    _check_workspace(workspace, img1.device)
     N, C, H, W = img1.shape
     rc = lib().ssim_loss_and_grad(_dptr(img1), _dptr(img2), _dtype_code(img1), N, C, H, W,
                                   _pad(padding), _dptr(dloss), _dptr(loss), _dptr(workspace),
@@ -358,8 +418,8 @@ def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute:
     (the default) the forward saves nothing but the images and the backward
     forms the statistics again from them; recompute=False saves the four
     blurred statistics (16 bytes per map entry) for the backward to read.
-    Both give the same gradient; the recomputing backward is as fast at 1080p
-    and faster on larger batches."""
+    Both give the same gradient; the recomputing backward is faster, at 1080p
+    and more so on larger batches."""
     global _fn
     if _fn is None:
         _fn = _make_function()
@@ -412,6 +472,7 @@ def ssim_reference_stats(img2, padding, ref) -> None:
     """Calls the C ``ssim_reference_stats`` on torch's current stream."""
     _check_image(img2, "img2")
     N, C, H, W = img2.shape
+    _check_buffer(ref, "ref", img2.device, ssim_reference_bytes(N, C, H, W, padding), _f32())
     rc = lib().ssim_reference_stats(_dptr(img2), _dtype_code(img2), N, C, H, W, _pad(padding),
                                     _dptr(ref), _stream_ptr(img2))
     if rc != SSIM_OK:
@@ -422,6 +483,9 @@ def ssim_loss_and_grad_ref(img1, img2, ref, padding, dloss, loss, workspace, gra
     """Calls the C ``ssim_loss_and_grad_ref`` on torch's current stream."""
     _check_pair_and_grads(img1, img2, (grad_img1,))
     N, C, H, W = img1.shape
+    _check_scalars(img1.device, dloss=dloss, loss=loss)
+    _check_buffer(ref, "ref", img1.device, ssim_reference_bytes(N, C, H, W, padding), _f32())
+    _check_workspace(workspace, img1.device)
     rc = lib().ssim_loss_and_grad_ref(_dptr(img1), _dptr(img2), _dptr(ref), _dtype_code(img1), N,
                                       C, H, W, _pad(padding), _dptr(dloss), _dptr(loss),
                                       _dptr(workspace), _dptr(grad_img1), _stream_ptr(img1))
@@ -483,6 +547,10 @@ def ssim3d_forward(vol1, vol2, padding, loss, saved_maps, workspace) -> None:
     may be None: inference)."""
     _check_pair_and_grads(vol1, vol2, (), ndim=5)
     N, C, D, H, W = vol1.shape
+    _check_scalars(vol1.device, loss=loss)
+    _check_buffer(saved_maps, "saved_maps", vol1.device,
+                  ssim3d_saved_maps_bytes(N, C, D, H, W, padding), _f32())
+    _check_workspace(workspace, vol1.device)
     rc = lib().ssim3d_forward(_dptr(vol1), _dptr(vol2), _dtype_code(vol1), N, C, D, H, W,
                               _pad(padding), _dptr(loss), _dptr(saved_maps), _dptr(workspace),
                               _stream_ptr(vol1))
@@ -494,6 +562,9 @@ def ssim3d_backward(dloss, vol1, vol2, padding, saved_maps, grad_vol1, grad_vol2
     """Calls the C ``ssim3d_backward`` on torch's current stream."""
     _check_pair_and_grads(vol1, vol2, (grad_vol1, grad_vol2), ndim=5)
     N, C, D, H, W = vol1.shape
+    _check_scalars(vol1.device, dloss=dloss)
+    _check_buffer(saved_maps, "saved_maps", vol1.device,
+                  ssim3d_saved_maps_bytes(N, C, D, H, W, padding), _f32())
     rc = lib().ssim3d_backward(_dptr(dloss), _dptr(vol1), _dptr(vol2), _dtype_code(vol1), N, C,
                                D, H, W, _pad(padding), _dptr(saved_maps), _dptr(grad_vol1),
                                _dptr(grad_vol2), _stream_ptr(vol1))

@@ -242,6 +242,37 @@ def test_python_binding_rejects_cpu_tensors():
         S.ssim_loss(x.half(), x.half())
 
 
+def test_python_binding_buffer_checks():
+    """The binding's checks of output and state buffers (run on host tensors,
+    with the host as the images' device)."""
+    import torch
+
+    cpu = torch.device("cpu")
+    S._check_buffer(None, "maps", cpu, 64, torch.float32)  # NULL: the C function decides
+    S._check_buffer(torch.empty(16), "maps", cpu, 64, torch.float32)
+    S._check_scalars(cpu, loss=torch.empty(()), dloss=torch.empty(1))
+    with pytest.raises(ValueError):
+        S._check_buffer(torch.empty(15), "maps", cpu, 64, torch.float32)
+    with pytest.raises(ValueError):
+        S._check_buffer(torch.empty(32)[::2], "maps", cpu, 64, torch.float32)
+    with pytest.raises(TypeError):
+        S._check_buffer(torch.empty(16, dtype=torch.float64), "maps", cpu, 64, torch.float32)
+    with pytest.raises(TypeError):
+        S._check_buffer(torch.empty(16), "maps", torch.device("cuda", 0), 64)
+    with pytest.raises(TypeError):
+        S._check_buffer(np.empty(16, np.float32), "maps", cpu, 64)
+    with pytest.raises(ValueError):
+        S._check_scalars(cpu, loss=torch.empty(0))
+    with pytest.raises(TypeError):
+        S._check_scalars(cpu, dloss=torch.empty((), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        S._check_workspace(torch.empty(S.ssim_workspace_bytes() - 1, dtype=torch.uint8), cpu)
+    x = torch.empty(1, 1, 4, 4)
+    S._check_grads(x, (None, torch.empty(1, 1, 4, 4)))
+    with pytest.raises(TypeError):
+        S._check_grads(x, (torch.empty(1, 1, 4, 5),))
+
+
 def test_build_entry_point_compiles_and_checks_the_abi():
     """__graft_entry__.build() compiles the library and the oracle in-tree
     (the atomic rename leaves the copy this process loaded intact) and checks

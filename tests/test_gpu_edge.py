@@ -361,6 +361,60 @@ def test_rejects_bad_inputs_on_gpu():
         S.ssim_loss(torch.rand(1, 1, 8, 32, device=dev), torch.rand(1, 1, 8, 32, device=dev), "valid")
 
 
+def test_rejects_bad_buffers_before_any_launch():
+    """Output and state buffers that the kernels would write or read out of
+    bounds (on the host, too small, strided, of the wrong type, or a second
+    image of another shape) are refused by the binding; nothing is launched,
+    so the good buffers keep the values they were filled with."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    a = torch.rand(1, 2, 24, 40, device=dev)
+    b = torch.rand(1, 2, 24, 40, device=dev)
+    ws = S.workspace_for(dev)
+    loss = torch.full((), 7.0, device=dev)
+    dl = torch.ones((), device=dev)
+    g1 = torch.full_like(a, 3.0)
+    g2 = torch.full_like(a, 3.0)
+    maps = S.alloc_saved_maps(a, "valid")
+    small_maps = maps[: maps.numel() - 4]
+    ref = S.reference_stats(b, "valid")
+    cases = {
+        "grad on the host": lambda: S.ssim_loss_and_grad(a, b, "valid", dl, loss, ws,
+                                                         torch.empty(a.shape), g2),
+        "strided grad": lambda: S.ssim_backward_recompute(
+            dl, a, b, "valid", torch.empty(1, 2, 24, 80, device=dev)[..., ::2], g2),
+        "grad of another dtype": lambda: S.ssim_backward_recompute(
+            dl, a, b, "valid", g1.double(), g2),
+        "loss on the host": lambda: S.ssim_forward(a, b, "valid", torch.empty(()), None, ws),
+        "fp64 loss": lambda: S.ssim_loss_and_grad(a, b, "valid", dl, loss.double(), ws, g1, g2),
+        "empty dloss": lambda: S.ssim_backward_recompute(torch.empty(0, device=dev), a, b,
+                                                         "valid", g1, g2),
+        "small workspace": lambda: S.ssim_forward(a, b, "valid", loss, None, ws[:4]),
+        "short saved maps (forward)": lambda: S.ssim_forward(a, b, "valid", loss, small_maps, ws),
+        "short saved maps (backward)": lambda: S.ssim_backward(dl, a, b, "valid", small_maps, g1,
+                                                               g2),
+        "maps of another padding": lambda: S.ssim_forward(a, b, "same", loss, maps, ws),
+        "second image of another shape": lambda: S.ssim_backward(
+            dl, a, b[:, :1], "valid", maps, g1, g2),
+        "short reference": lambda: S.ssim_loss_and_grad_ref(a, b, ref[:-1], "valid", dl, loss,
+                                                             ws, g1),
+        "volume maps short": lambda: S.ssim3d_forward(
+            a.reshape(1, 1, 2, 24, 40), b.reshape(1, 1, 2, 24, 40), "same", loss,
+            torch.empty(4, device=dev), ws),
+    }
+    torch.cuda.synchronize()
+    for name, call in cases.items():
+        say(f"[edge] bad buffer: {name}")
+        with pytest.raises((TypeError, ValueError)):
+            call()
+    torch.cuda.synchronize()
+    assert float(loss.item()) == 7.0
+    assert bool((g1 == 3.0).all()) and bool((g2 == 3.0).all())
+
+
 def test_maximum_plane_size():
     """Two planes of 2^27 elements (8192 x 16384, the documented limit; 1 GiB
     per tensor): the one-launch step (whose strips span both planes behind one
