@@ -165,10 +165,23 @@ def ssim_workspace_bytes() -> int:
 
 
 # --------------------------------------------------------------------------- device calls
-def _stream_ptr(t) -> int:
-    import torch
+_raw_stream = None
 
-    return torch.cuda.current_stream(t.device).cuda_stream
+
+def _current_stream(index: int) -> int:
+    """The raw HIP stream torch's current stream on device `index` wraps (the
+    accessor without a Python stream object: a few hundredths of the cost)."""
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None) or (
+            lambda i: torch.cuda.current_stream(i).cuda_stream)
+    return _raw_stream(index)
+
+
+def _stream_ptr(t) -> int:
+    return _current_stream(t.device.index)
 
 
 def _dptr(t):
@@ -348,10 +361,12 @@ def workspace_for(device) -> "torch.Tensor":
     import torch
 
     dev = torch.device(device)
-    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (index, _current_stream(index))
     ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.zeros(ssim_workspace_bytes(), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(ssim_workspace_bytes(), dtype=torch.uint8,
+                         device=torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
 
@@ -439,6 +454,16 @@ def fused_ssim(img1, img2, padding: str = "same", train: bool = True):
     return 1.0 - ssim_loss(img1, img2, padding, train)
 
 
+def _dloss_tensor(weight, dev):
+    """The upstream gradient as a 0-d fp32 device tensor.  A number is filled
+    in on the stream (a copy from the host would wait for it)."""
+    import torch
+
+    if isinstance(weight, torch.Tensor):
+        return weight.detach().to(device=dev, dtype=torch.float32).reshape(()).contiguous()
+    return torch.full((), float(weight), dtype=torch.float32, device=dev)
+
+
 def loss_and_grad(img1, img2, padding: str = "valid", weight=1.0, grad1: bool = True,
                   grad2: bool = True):
     """One launch for a training step whose upstream gradient is known before
@@ -450,10 +475,7 @@ def loss_and_grad(img1, img2, padding: str = "valid", weight=1.0, grad1: bool = 
 
     _check_pair_and_grads(img1, img2, ())
     dev = img1.device
-    if isinstance(weight, torch.Tensor):
-        dl = weight.detach().to(device=dev, dtype=torch.float32).reshape(()).contiguous()
-    else:
-        dl = torch.tensor(float(weight), dtype=torch.float32, device=dev)
+    dl = _dloss_tensor(weight, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     g1 = torch.empty_like(img1) if grad1 else None
     g2 = torch.empty_like(img2) if grad2 else None
@@ -514,10 +536,7 @@ def loss_and_grad_ref(img1, img2, ref, padding: str = "valid", weight=1.0, grad1
 
     _check_pair_and_grads(img1, img2, ())
     dev = img1.device
-    if isinstance(weight, torch.Tensor):
-        dl = weight.detach().to(device=dev, dtype=torch.float32).reshape(()).contiguous()
-    else:
-        dl = torch.tensor(float(weight), dtype=torch.float32, device=dev)
+    dl = _dloss_tensor(weight, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     g1 = torch.empty_like(img1) if grad1 else None
     ssim_loss_and_grad_ref(img1.detach(), img2.detach(), ref, padding, dl, loss,
