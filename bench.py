@@ -67,9 +67,31 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with a cache flush before each (0 = skip)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="before the warmup steps, run untimed steps for at least this long "
+                         "(an idle GPU needs some milliseconds of load to reach its clock)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (counter calibration)")
     return ap.parse_args()
+
+
+def settle(step, ms):
+    """Untimed steps until at least `ms` milliseconds of them have run: a GPU
+    that sat idle (while the host built the inputs) takes several milliseconds
+    of load to reach its clock, longer than a few dozen short warmup steps
+    last.  Synchronised every 10 steps, so the host never queues far ahead.
+    Returns the number of steps run."""
+    import torch
+
+    n = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    return n
 
 
 _CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
@@ -261,13 +283,18 @@ def bench_volume(args, w, x, y):
     g2 = torch.empty_like(t2)
     fwd = lambda: S.ssim3d_forward(t1, t2, w.padding, loss, maps, ws)
     bwd = lambda: S.ssim3d_backward(dloss, t1, t2, w.padding, maps, g1, g2)
+    def vstep():
+        fwd()
+        bwd()
+
+    n_settle = settle(vstep, args.settle_ms)
     for _ in range(args.warmup):
-        fwd(); bwd()
+        vstep()
     torch.cuda.synchronize()
     K = args.steps
     t0 = time.perf_counter()
     for _ in range(K):
-        fwd(); bwd()
+        vstep()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     mvox = N * D * H * W / 1e6
@@ -297,6 +324,7 @@ def bench_volume(args, w, x, y):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": n_settle},
         "ms_per_step": round(elapsed * 1e3 / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -384,6 +412,7 @@ def main():
         for f in step_launches:
             f()
 
+    n_settle = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -512,6 +541,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": n_settle},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
