@@ -448,9 +448,10 @@ def main():
              and (args.all_kernels or k in DESIGNS[args.design])]
     kern = {k: per_launch_ms(launches[k]) for k in timed}
 
-    # the autograd path (ssim_loss(...).backward(): inference forward, then
-    # the recomputing backward, with torch's autograd bookkeeping), timed
-    # with events around K whole steps
+    # the autograd path (ssim_loss(...).backward() on fp32 images: the
+    # one-launch kernel with an upstream gradient of 1 in the forward, the
+    # gradient scaled in the backward, with torch's autograd bookkeeping),
+    # timed with events around K whole steps
     autograd = None
     if args.all_kernels and args.dtype == "float32":
         a1 = t1.detach().clone().requires_grad_(True)
@@ -464,7 +465,7 @@ def main():
         torch.cuda.synchronize()
         ag_ms = per_launch_ms(ag_step)
         autograd = {"ms_per_step": round(ag_ms, 5), "mpix_per_s": round(mpix / (ag_ms * 1e-3), 1),
-                    "launches": "ssim_forward (inference) + ssim_backward_recompute"}
+                    "launches": "ssim_loss_and_grad (upstream gradient 1) + ssim_grad_scale"}
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 6
+#define SSIM_ABI_VERSION 7
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -197,6 +197,29 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
 int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
                        int64_t H, int64_t W, int padding, const float* dloss, float* loss,
                        void* workspace, void* grad_img1, void* grad_img2, void* stream);
+
+/* The chain rule's last factor, applied later: out[i] = *dloss * grad[i] for
+ * 0 <= i < n, fp32.  "TriSSIM", How it works: the backward multiplies the
+ * loss's own gradient by the upstream gradient.  A caller that does not know
+ * the upstream gradient at the forward (an autograd step) runs
+ * ssim_loss_and_grad there with *dloss = 1 and this call in the backward.
+ * The kernels form a gradient as *dloss times an fp32 value, and with
+ * *dloss = 1 they store that value exactly, so the result equals
+ * ssim_loss_and_grad's with the same *dloss bit for bit (fp32 gradients; a
+ * half-precision gradient would be rounded twice).
+ *
+ *   dloss  : device fp32 scalar, the upstream gradient
+ *   grad   : device fp32 array of n elements (input), 4-byte aligned
+ *   out    : device fp32 array of n elements (output, overwritten); may be
+ *            grad itself (in place), must not otherwise overlap it
+ *   n      : element count; 0 launches nothing
+ *   stream : hipStream_t (NULL = default stream)
+ * Returns SSIM_ERR_SHAPE for n < 0 or a pointer not 4-byte aligned,
+ * SSIM_ERR_NULL for a NULL pointer with n > 0, SSIM_ERR_OVERFLOW when 4 n
+ * bytes overflow and SSIM_ERR_ALIAS for a partial overlap, all before any
+ * HIP call; SSIM_ERR_DEVICE on a device that is not gfx950; SSIM_ERR_HIP if
+ * the launch fails. */
+int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Cached reference statistics.  In a training run the second image is often

@@ -13,13 +13,16 @@ are called for the half types):
   ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2)
   ssim_backward_recompute(dloss, img1, img2, padding, grad_img1, grad_img2)
   ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, grad_img2)
+  ssim_grad_scale(dloss, grad, out)
   ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
   ssim_strerror, ssim_abi_version
 Autograd conveniences ("TriSSIM" / "Fully Fused Differentiable SSIM", Usage):
   ssim_loss(img1, img2, padding="valid", train=True, recompute=True)
       -> 1 - mean SSIM; by default no maps are kept between forward and
-         backward (the backward forms the statistics again from the images);
-         recompute=False saves them
+         backward: for fp32 images the forward forms the loss and the
+         gradients in one launch and the backward scales them by the upstream
+         gradient; for half types the backward forms the statistics again
+         from the images.  recompute=False saves the statistics
   fused_ssim(img1, img2, padding="same", train=True)  -> mean SSIM
 One-pass step, for an upstream gradient known in advance:
   loss_and_grad(img1, img2, padding="valid", weight=1.0)
@@ -44,7 +47,7 @@ from .build import LIB_PATH
 
 # SSIM_ABI_VERSION of include/ssim_loss_amd.h that these bindings follow; a
 # library built from another version is refused at load time
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 PAD = {"valid": 0, "same": 1}
 SSIM_OK = 0
@@ -118,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.ssim_loss_and_grad_ref.restype = i32
         L.ssim_loss_and_grad_ref.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i32, vp, vp,
                                              vp, vp, vp]
+        L.ssim_grad_scale.restype = i32
+        L.ssim_grad_scale.argtypes = [vp, vp, vp, i64, vp]
         L.ssim_loss_and_grad.restype = i32
         L.ssim_loss_and_grad.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                          vp]
@@ -349,6 +354,25 @@ def ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, g
         raise SsimError(rc, "ssim_loss_and_grad")
 
 
+def ssim_grad_scale(dloss, grad, out) -> None:
+    """Calls the C ``ssim_grad_scale`` (out = *dloss * grad, fp32) on torch's
+    current stream; out may be grad itself."""
+    import torch
+
+    if not isinstance(grad, torch.Tensor) or grad.device.type != "cuda":
+        raise TypeError("grad must be a GPU tensor")
+    if grad.dtype != torch.float32 or not grad.is_contiguous():
+        raise TypeError("grad must be a contiguous float32 tensor")
+    _check_buffer(out, "out", grad.device, grad.nbytes, torch.float32)
+    if out is None or out.numel() != grad.numel():
+        raise ValueError("out must have grad's number of elements")
+    _check_scalars(grad.device, dloss=dloss)
+    rc = lib().ssim_grad_scale(_dptr(dloss), _dptr(grad), _dptr(out), grad.numel(),
+                               _stream_ptr(grad))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_grad_scale")
+
+
 # --------------------------------------------------------------------------- buffers
 _workspaces: dict = {}
 
@@ -387,15 +411,28 @@ def _make_function():
 
     class _SsimLoss(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, img1, img2, padding, train, recompute):
+        def forward(ctx, img1, img2, padding, train, recompute, grads):
             img1 = img1.detach()
             img2 = img2.detach()
-            loss = torch.empty((), dtype=torch.float32, device=img1.device)
-            maps = alloc_saved_maps(img1, padding) if train and not recompute else None
-            ssim_forward(img1, img2, padding, loss, maps, workspace_for(img1.device))
+            dev = img1.device
+            loss = torch.empty((), dtype=torch.float32, device=dev)
             ctx.padding = padding
             ctx.train = train
             ctx.recompute = recompute
+            # fp32 images whose gradient is wanted: the gradients with an
+            # upstream gradient of 1, in the launch that forms the loss; the
+            # backward only scales them (bit for bit the one-launch result)
+            ctx.early = bool(train and recompute and grads and img1.dtype == torch.float32)
+            if ctx.early:
+                want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+                g1 = torch.empty_like(img1) if want1 else None
+                g2 = torch.empty_like(img2) if want2 else None
+                ssim_loss_and_grad(img1, img2, padding, _one(dev), loss, workspace_for(dev), g1,
+                                   g2)
+                ctx.save_for_backward(g1, g2)
+                return loss
+            maps = alloc_saved_maps(img1, padding) if train and not recompute else None
+            ssim_forward(img1, img2, padding, loss, maps, workspace_for(dev))
             if train:
                 if recompute:
                     ctx.save_for_backward(img1, img2)
@@ -409,6 +446,16 @@ def _make_function():
                 raise RuntimeError("ssim_loss was called with train=False; no gradient saved")
             want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
             dl = dloss.detach().to(dtype=torch.float32).contiguous()
+            if ctx.early:
+                e1, e2 = ctx.saved_tensors
+                outs = []
+                for want, e in ((want1, e1), (want2, e2)):
+                    g = None
+                    if want and e is not None:
+                        g = torch.empty_like(e)
+                        ssim_grad_scale(dl, e, g)
+                    outs.append(g)
+                return outs[0], outs[1], None, None, None, None
             if ctx.recompute:
                 img1, img2 = ctx.saved_tensors
                 g1 = torch.empty_like(img1) if want1 else None
@@ -419,7 +466,7 @@ def _make_function():
                 g1 = torch.empty_like(img1) if want1 else None
                 g2 = torch.empty_like(img2) if want2 else None
                 ssim_backward(dl, img1, img2, ctx.padding, maps, g1, g2)
-            return g1, g2, None, None, None
+            return g1, g2, None, None, None, None
 
     return _SsimLoss
 
@@ -430,11 +477,15 @@ _fn = None
 def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute: bool = True):
     """loss = 1 - mean SSIM (a 0-d fp32 tensor on the images' device), with
     gradients for whichever of img1 / img2 requires them.  With recompute
-    (the default) the forward saves nothing but the images and the backward
-    forms the statistics again from them; recompute=False saves the four
-    blurred statistics (16 bytes per map entry) for the backward to read.
-    Both give the same gradient; the recomputing backward is faster, at 1080p
-    and more so on larger batches."""
+    (the default) no blurred statistics are kept between forward and
+    backward.  For fp32 images whose gradient is wanted, the forward forms
+    the loss and the gradients (for an upstream gradient of 1) in one launch
+    and the backward multiplies them by the upstream gradient, giving
+    ssim_loss_and_grad's result bit for bit; otherwise the forward forms the
+    loss alone and the backward forms the statistics again from the images.
+    recompute=False saves the four blurred statistics (16 bytes per map
+    entry) for the backward to read, as the pages' training mode does.  All
+    three give the same gradient to the contract's tolerance."""
     global _fn
     if _fn is None:
         _fn = _make_function()
@@ -445,13 +496,32 @@ def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute:
     if img1.dtype != img2.dtype:
         raise TypeError("img1 and img2 must have the same dtype")
     _pad(padding)
-    return _fn.apply(img1, img2, padding, bool(train), bool(recompute))
+    import torch
+
+    grads = torch.is_grad_enabled() and (img1.requires_grad or img2.requires_grad)
+    return _fn.apply(img1, img2, padding, bool(train), bool(recompute), grads)
 
 
 def fused_ssim(img1, img2, padding: str = "same", train: bool = True):
     """Mean SSIM ("Fully Fused Differentiable SSIM", Usage: default padding
     "same")."""
     return 1.0 - ssim_loss(img1, img2, padding, train)
+
+
+_ones: dict = {}
+
+
+def _one(dev):
+    """A 0-d fp32 1.0 on `dev`, made once per device (read only).  It is
+    copied from the host, which waits for the copy, so that calls on any
+    stream may read it afterwards."""
+    import torch
+
+    one = _ones.get(dev)
+    if one is None:
+        one = torch.ones((), dtype=torch.float32).to(dev)
+        _ones[dev] = one
+    return one
 
 
 def _dloss_tensor(weight, dev):

@@ -85,6 +85,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int elem_bytes(int dtype) { return dtype == SSIM_DTYPE_F32 ? 4 : 2; }
+
+// out = *dloss * grad over n fp32 elements, grid-stride; kVec: both arrays
+// 16-byte aligned, four elements per load and store, the last n % 4 one at a
+// time.  The product is the one the gradient kernels form last.
+constexpr int kScaleThreads = 256;
+template <bool kVec>
+__global__ __launch_bounds__(kScaleThreads) void ssim_grad_scale_kernel(const float* dloss,
+                                                                        const float* grad,
+                                                                        float* out, int64_t n) {
+  const float s = *dloss;
+  const int64_t stride = (int64_t)gridDim.x * kScaleThreads;
+  const int64_t i0 = (int64_t)blockIdx.x * kScaleThreads + threadIdx.x;
+  int64_t done = 0;
+  if constexpr (kVec) {
+    const int64_t n4 = n >> 2;
+    const float4* g4 = reinterpret_cast<const float4*>(grad);
+    float4* o4 = reinterpret_cast<float4*>(out);
+    for (int64_t k = i0; k < n4; k += stride) {
+      const float4 v = g4[k];
+      o4[k] = make_float4(s * v.x, s * v.y, s * v.z, s * v.w);
+    }
+    done = n4 << 2;
+  }
+  for (int64_t k = done + i0; k < n; k += stride) out[k] = s * grad[k];
+}
 // an image or gradient pointer must be aligned to its element size
 bool misaligned(const void* ptr, int dtype) {
   return ((uintptr_t)ptr % (uintptr_t)elem_bytes(dtype)) != 0;
@@ -635,6 +660,34 @@ int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N,
   if (!loss) return SSIM_ERR_NULL;
   return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
                         grad_img2, stream);
+}
+
+int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n, void* stream) {
+  if (n < 0) return SSIM_ERR_SHAPE;
+  if (n == 0) return SSIM_OK;
+  if (!dloss || !grad || !out) return SSIM_ERR_NULL;
+  if (n > INT64_MAX / 4) return SSIM_ERR_OVERFLOW;
+  if (((uintptr_t)grad | (uintptr_t)out | (uintptr_t)dloss) % 4 != 0) return SSIM_ERR_SHAPE;
+  const size_t bytes = (size_t)n * 4;
+  if ((const void*)out != (const void*)grad && overlaps(out, bytes, grad, bytes))
+    return SSIM_ERR_ALIAS;
+  const DeviceInfo* d = nullptr;
+  const int rc = device_info(&d);
+  if (rc != SSIM_OK) return rc;
+  const bool vec = ((uintptr_t)grad | (uintptr_t)out) % 16 == 0;
+  const int64_t units = vec ? (n >> 2) + (n & 3) : n;
+  int64_t G = (units + kScaleThreads - 1) / kScaleThreads;
+  const int64_t cap = (int64_t)d->cus * 8;
+  if (G > cap) G = cap;
+  if (G < 1) G = 1;
+  const hipStream_t st = (hipStream_t)stream;
+  if (vec)
+    ssim_grad_scale_kernel<true><<<dim3((unsigned)G), dim3(kScaleThreads), 0, st>>>(dloss, grad,
+                                                                                     out, n);
+  else
+    ssim_grad_scale_kernel<false><<<dim3((unsigned)G), dim3(kScaleThreads), 0, st>>>(dloss, grad,
+                                                                                      out, n);
+  return hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
 }
 
 size_t ssim_reference_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding) {

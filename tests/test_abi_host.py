@@ -180,6 +180,20 @@ def test_loss_and_grad_argument_errors_return_before_any_hip_call():
     assert _lag(lib, loss=0x300000 + 8) == -5       # loss inside the workspace
 
 
+def test_grad_scale_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    f = lambda dl, g, o, n: lib.ssim_grad_scale(dl, g, o, n, None)
+    assert f(None, None, None, 0) == 0                   # nothing to do: no launch
+    assert f(0x1000, 0x10000, 0x20000, -1) == -2
+    assert f(None, 0x10000, 0x20000, 8) == -1
+    assert f(0x1000, None, 0x20000, 8) == -1
+    assert f(0x1000, 0x10000, None, 8) == -1
+    assert f(0x1000, 0x10002, 0x20000, 8) == -2          # not 4-byte aligned
+    assert f(0x1000, 0x10000, 0x10000 + 16, 8) == -5     # partial overlap
+    assert f(0x1000, 0x10000, 0x10000 - 16, 8) == -5
+    assert f(0x1000, 0x10000, 0x20000, 1 << 62) == -4
+
+
 def test_reference_argument_errors_return_before_any_hip_call():
     lib = S.lib()
     assert S.ssim_reference_bytes(1, 3, 1080, 1920, "valid") == 4 * 3 * 1070 * 1912

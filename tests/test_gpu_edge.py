@@ -190,6 +190,80 @@ def test_autograd_functions(recompute):
     assert abs(float(v.item()) - (1 - sl)) <= 1e-5 * abs(sl)
 
 
+def test_grad_scale_is_the_fp32_product():
+    """ssim_grad_scale: out = *dloss * grad, element for element the fp32
+    product, for ragged lengths, 4-byte (not 16-byte) aligned arrays and in
+    place; n = 0 launches nothing."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(31)
+    for n, off_g, off_o in [(1, 0, 0), (3, 0, 0), (4, 0, 0), (1023, 0, 0), (4097, 1, 3),
+                            (6220800, 0, 0), (6220803, 2, 0), (0, 0, 0)]:
+        say(f"[scale] n={n} offsets {off_g} {off_o}")
+        g = rng.standard_normal(n + 4).astype(np.float32)
+        s = np.float32(rng.uniform(-3, 3))
+        tg = torch.from_numpy(g).to(dev)
+        out = torch.full((n + 4,), 7.0, device=dev)
+        dl = torch.tensor(float(s), dtype=torch.float32, device=dev)
+        S.ssim_grad_scale(dl, tg[off_g:off_g + n], out[off_o:off_o + n])
+        res = out.cpu().numpy()
+        want = s * g[off_g:off_g + n]
+        assert np.array_equal(res[off_o:off_o + n], want)
+        assert (res[:off_o] == 7.0).all() and (res[off_o + n:] == 7.0).all()
+        S.ssim_grad_scale(dl, tg[:n], tg[:n])  # in place
+        assert np.array_equal(tg[:n].cpu().numpy(), s * g[:n])
+    with pytest.raises(S.SsimError):
+        a = torch.zeros(64, device=dev)
+        S.ssim_grad_scale(torch.ones((), device=dev), a[:32], a[16:48])
+
+
+@pytest.mark.parametrize("which", ["both", "img1", "img2"])
+def test_autograd_fp32_matches_the_one_launch_step_bit_for_bit(which):
+    """fp32 autograd (the forward forms the gradients with an upstream
+    gradient of 1, the backward scales them): the gradients equal
+    ssim_loss_and_grad's with the same upstream gradient bit for bit, for
+    either image or both, and a second backward through a retained graph
+    gives them again."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    say(f"[api] autograd fp32 early gradients, {which}")
+    x, y = make_pair((2, 3, 70, 300), "uniform", 0.1, seed=15)
+    dev = torch.device("cuda")
+    t1 = torch.from_numpy(x).to(dev).requires_grad_(which in ("both", "img1"))
+    t2 = torch.from_numpy(y).to(dev).requires_grad_(which in ("both", "img2"))
+    loss = S.ssim_loss(t1, t2, "valid")
+    w = torch.tensor(-0.37, device=dev)
+    (w * loss).backward(retain_graph=True)
+    l_ref, g1_ref, g2_ref = S.loss_and_grad(t1.detach(), t2.detach(), "valid", weight=w)
+    torch.cuda.synchronize()
+    ol, o1, o2 = oracle.ssim_loss(x, y, "valid", dloss=-0.37)
+    check_loss(float(loss.item()), ol)
+    assert float(loss.item()) == float(l_ref.item())
+    for t, ref, o in ((t1, g1_ref, o1), (t2, g2_ref, o2)):
+        if t.requires_grad:
+            assert torch.equal(t.grad, ref)
+            check_grad(t.grad.cpu().numpy(), o)
+        else:
+            assert t.grad is None
+    first = [t.grad.clone() if t.grad is not None else None for t in (t1, t2)]
+    for t in (t1, t2):
+        t.grad = None
+    (w * loss).backward()
+    for t, f in zip((t1, t2), first):
+        assert (t.grad is None) == (f is None)
+        if f is not None:
+            assert torch.equal(t.grad, f)
+    # without grad mode the forward forms the loss alone
+    with torch.no_grad():
+        v = S.ssim_loss(t1, t2, "valid")
+    check_loss(float(v.item()), ol)
+
+
 def test_workspace_reuse_across_shapes():
     """The completion counter is reset by every forward, so one workspace
     serves calls of any size in sequence."""
