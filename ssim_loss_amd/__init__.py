@@ -419,6 +419,7 @@ def _make_function():
             ctx.padding = padding
             ctx.train = train
             ctx.recompute = recompute
+            ctx.dev = dev
             # fp32 images whose gradient is wanted: the gradients with an
             # upstream gradient of 1, in the launch that forms the loss; the
             # backward only scales them (bit for bit the one-launch result)
@@ -427,8 +428,14 @@ def _make_function():
                 want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
                 g1 = torch.empty_like(img1) if want1 else None
                 g2 = torch.empty_like(img2) if want2 else None
-                ssim_loss_and_grad(img1, img2, padding, _one(dev), loss, workspace_for(dev), g1,
-                                   g2)
+                # ssim_loss checked the images; the other buffers are made here
+                N, C, H, W = img1.shape
+                rc = lib().ssim_loss_and_grad(
+                    img1.data_ptr(), img2.data_ptr(), SSIM_DTYPE["float32"], N, C, H, W,
+                    _pad(padding), _one(dev).data_ptr(), loss.data_ptr(),
+                    workspace_for(dev).data_ptr(), _dptr(g1), _dptr(g2), _current_stream(dev.index))
+                if rc != SSIM_OK:
+                    raise SsimError(rc, "ssim_loss_and_grad")
                 ctx.save_for_backward(g1, g2)
                 return loss
             maps = alloc_saved_maps(img1, padding) if train and not recompute else None
@@ -445,7 +452,7 @@ def _make_function():
             if not ctx.train:
                 raise RuntimeError("ssim_loss was called with train=False; no gradient saved")
             want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
-            dl = dloss.detach().to(dtype=torch.float32).contiguous()
+            dl = dloss.detach().to(device=ctx.dev, dtype=torch.float32).reshape(()).contiguous()
             if ctx.early:
                 e1, e2 = ctx.saved_tensors
                 outs = []
@@ -453,7 +460,10 @@ def _make_function():
                     g = None
                     if want and e is not None:
                         g = torch.empty_like(e)
-                        ssim_grad_scale(dl, e, g)
+                        rc = lib().ssim_grad_scale(dl.data_ptr(), e.data_ptr(), g.data_ptr(),
+                                                   e.numel(), _current_stream(e.device.index))
+                        if rc != SSIM_OK:
+                            raise SsimError(rc, "ssim_grad_scale")
                     outs.append(g)
                 return outs[0], outs[1], None, None, None, None
             if ctx.recompute:
