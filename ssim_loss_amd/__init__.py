@@ -439,7 +439,13 @@ def _make_function():
                 ctx.save_for_backward(g1, g2)
                 return loss
             maps = alloc_saved_maps(img1, padding) if train and not recompute else None
-            ssim_forward(img1, img2, padding, loss, maps, workspace_for(dev))
+            N, C, H, W = img1.shape
+            rc = lib().ssim_forward_typed(
+                img1.data_ptr(), img2.data_ptr(), _dtype_code(img1), N, C, H, W, _pad(padding),
+                loss.data_ptr(), _dptr(maps), workspace_for(dev).data_ptr(),
+                _current_stream(dev.index))
+            if rc != SSIM_OK:
+                raise SsimError(rc, "ssim_forward")
             if train:
                 if recompute:
                     ctx.save_for_backward(img1, img2)
@@ -468,14 +474,24 @@ def _make_function():
                 return outs[0], outs[1], None, None, None, None
             if ctx.recompute:
                 img1, img2 = ctx.saved_tensors
-                g1 = torch.empty_like(img1) if want1 else None
-                g2 = torch.empty_like(img2) if want2 else None
-                ssim_backward_recompute(dl, img1, img2, ctx.padding, g1, g2)
             else:
                 img1, img2, maps = ctx.saved_tensors
-                g1 = torch.empty_like(img1) if want1 else None
-                g2 = torch.empty_like(img2) if want2 else None
-                ssim_backward(dl, img1, img2, ctx.padding, maps, g1, g2)
+            g1 = torch.empty_like(img1) if want1 else None
+            g2 = torch.empty_like(img2) if want2 else None
+            N, C, H, W = img1.shape
+            stream = _current_stream(ctx.dev.index)
+            if ctx.recompute:
+                rc = lib().ssim_backward_recompute(
+                    dl.data_ptr(), img1.data_ptr(), img2.data_ptr(), _dtype_code(img1), N, C, H, W,
+                    _pad(ctx.padding), _dptr(g1), _dptr(g2), stream)
+                where = "ssim_backward_recompute"
+            else:
+                rc = lib().ssim_backward_typed(
+                    dl.data_ptr(), img1.data_ptr(), img2.data_ptr(), _dtype_code(img1), N, C, H, W,
+                    _pad(ctx.padding), maps.data_ptr(), _dptr(g1), _dptr(g2), stream)
+                where = "ssim_backward"
+            if rc != SSIM_OK:
+                raise SsimError(rc, where)
             return g1, g2, None, None, None, None
 
     return _SsimLoss
