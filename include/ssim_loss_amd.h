@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSIM_ABI_VERSION 7
+#define SSIM_ABI_VERSION 8
 
 /* padding ("Fully Fused Differentiable SSIM", Usage) */
 enum {
@@ -61,7 +61,9 @@ enum {
   SSIM_ERR_ALIAS = -5,    /* an output buffer overlaps an input or another output */
   SSIM_ERR_HIP = -6,      /* a HIP runtime call failed (launch, device query) */
   SSIM_ERR_DEVICE = -7,   /* the current device is not a wave64 gfx950 GPU */
-  SSIM_ERR_DTYPE = -8     /* dtype is not one of SSIM_DTYPE_* */
+  SSIM_ERR_DTYPE = -8,    /* dtype is not one of SSIM_DTYPE_* */
+  SSIM_ERR_SCRATCH = -9   /* the call needs more scratch than the library's fixed device
+                             array holds (ssim_loss_and_grad_noalloc) */
 };
 
 /* storage type of images and gradients for the _typed entry points; the
@@ -197,6 +199,41 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
 int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N, int64_t C,
                        int64_t H, int64_t W, int padding, const float* dloss, float* loss,
                        void* workspace, void* grad_img1, void* grad_img2, void* stream);
+
+/* Allocation-free variant of ssim_loss_and_grad, for callers that cannot
+ * allocate device memory or own a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * result as ssim_loss_and_grad without `workspace`; the loss accumulator
+ * lives instead in a device array inside the library,
+ * ssim_noalloc_scratch_bytes() bytes on each GPU it runs on, held until the
+ * process ends.  Every shape the step accepts needs one accumulator (8 bytes
+ * used of that array), so no shape exceeds it; SSIM_ERR_SCRATCH would report
+ * a need beyond it.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); the first call on a device, with that device current,
+ * looks up the array's address and clears the array with a small kernel on
+ * `stream` ahead of its own launch.  Each launch leaves the accumulator at
+ * zero when it completes.
+ *
+ * All calls on one GPU share that GPU's array: two calls that may run at the
+ * same time on one GPU (different streams without ordering between them)
+ * race on it and may both write a wrong loss.  Calls on one stream, or
+ * ordered by events, are safe.
+ *
+ *   img1, img2   : device images of `dtype` (inputs)
+ *   dtype, N..padding : as for ssim_forward_typed
+ *   dloss        : device fp32 scalar, read before any gradient is formed
+ *   loss         : device fp32 scalar (output; required)
+ *   grad_img1/2  : device outputs of `dtype`, or NULL to skip
+ *   stream       : hipStream_t (NULL = default stream)
+ * Argument checks and codes as for ssim_loss_and_grad, all before any HIP
+ * call. */
+int ssim_loss_and_grad_noalloc(const void* img1, const void* img2, int dtype, int64_t N,
+                               int64_t C, int64_t H, int64_t W, int padding, const float* dloss,
+                               float* loss, void* grad_img1, void* grad_img2, void* stream);
+
+/* Bytes of the per-GPU scratch array ssim_loss_and_grad_noalloc uses (256).
+ * Host-only. */
+size_t ssim_noalloc_scratch_bytes(void);
 
 /* The chain rule's last factor, applied later: out[i] = *dloss * grad[i] for
  * 0 <= i < n, fp32.  "TriSSIM", How it works: the backward multiplies the

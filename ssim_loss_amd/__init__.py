@@ -13,6 +13,7 @@ are called for the half types):
   ssim_backward(dloss, img1, img2, padding, saved_maps, grad_img1, grad_img2)
   ssim_backward_recompute(dloss, img1, img2, padding, grad_img1, grad_img2)
   ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, grad_img2)
+  ssim_loss_and_grad_noalloc(img1, img2, padding, dloss, loss, grad_img1, grad_img2)
   ssim_grad_scale(dloss, grad, out)
   ssim_saved_maps_bytes, ssim_workspace_bytes, ssim_map_shape, ssim_taps,
   ssim_strerror, ssim_abi_version
@@ -47,7 +48,7 @@ from .build import LIB_PATH
 
 # SSIM_ABI_VERSION of include/ssim_loss_amd.h that these bindings follow; a
 # library built from another version is refused at load time
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 PAD = {"valid": 0, "same": 1}
 SSIM_OK = 0
@@ -126,6 +127,11 @@ def lib() -> ctypes.CDLL:
         L.ssim_loss_and_grad.restype = i32
         L.ssim_loss_and_grad.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
                                          vp]
+        L.ssim_loss_and_grad_noalloc.restype = i32
+        L.ssim_loss_and_grad_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp, vp,
+                                                 vp, vp]
+        L.ssim_noalloc_scratch_bytes.restype = sz
+        L.ssim_noalloc_scratch_bytes.argtypes = []
         _lib = L
     return _lib
 
@@ -352,6 +358,25 @@ def ssim_loss_and_grad(img1, img2, padding, dloss, loss, workspace, grad_img1, g
                                   _dptr(grad_img1), _dptr(grad_img2), _stream_ptr(img1))
     if rc != SSIM_OK:
         raise SsimError(rc, "ssim_loss_and_grad")
+
+
+def ssim_loss_and_grad_noalloc(img1, img2, padding, dloss, loss, grad_img1, grad_img2) -> None:
+    """Calls the C ``ssim_loss_and_grad_noalloc`` (the one-launch step with
+    the loss accumulator in the library's own device array: no workspace) on
+    torch's current stream.  Calls that may overlap on one GPU race on that
+    array."""
+    _check_pair_and_grads(img1, img2, (grad_img1, grad_img2))
+    _check_scalars(img1.device, dloss=dloss, loss=loss)
+    N, C, H, W = img1.shape
+    rc = lib().ssim_loss_and_grad_noalloc(_dptr(img1), _dptr(img2), _dtype_code(img1), N, C, H,
+                                          W, _pad(padding), _dptr(dloss), _dptr(loss),
+                                          _dptr(grad_img1), _dptr(grad_img2), _stream_ptr(img1))
+    if rc != SSIM_OK:
+        raise SsimError(rc, "ssim_loss_and_grad_noalloc")
+
+
+def ssim_noalloc_scratch_bytes() -> int:
+    return int(lib().ssim_noalloc_scratch_bytes())
 
 
 def ssim_grad_scale(dloss, grad, out) -> None:

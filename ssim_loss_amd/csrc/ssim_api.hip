@@ -78,6 +78,57 @@ int device_info(const DeviceInfo** out) {
 
 int64_t roundup4(int64_t v) { return (v + 3) & ~(int64_t)3; }
 
+// Scratch of the allocation-free entry point (ssim_loss_and_grad_noalloc):
+// the one-launch step's only memory beyond its inputs and outputs is the
+// loss accumulator (a Workspace), which here lives in a file-scope device
+// array instead of a caller's buffer.  Each GPU holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = 256;
+static_assert(sizeof(Workspace) <= kScratchBytes, "the accumulator fits the scratch array");
+static __device__ __align__(256) unsigned long long scratch[kScratchBytes / 8];
+
+struct ScratchInfo {
+  bool ready = false;
+  int status = SSIM_OK;
+  void* ptr = nullptr;  // this device's copy of `scratch`
+};
+ScratchInfo g_scratch[kMaxDevices];
+
+// zero n 64-bit words (a plain kernel, so that a caller capturing the stream
+// records a kernel node rather than a memset)
+__global__ __launch_bounds__(64) void ssim_zero_words_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+// This device's scratch address.  The first call on a device, with that
+// device current, resolves it and clears the array on `stream` (ahead of the
+// call's own launch on the same stream); later calls reuse the address.  The
+// kernels leave the accumulator at zero when they finish, so it stays clear.
+int scratch_for_device(void* stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSIM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSIM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  ScratchInfo& s = g_scratch[dev];
+  if (!s.ready) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      s.status = SSIM_ERR_HIP;
+    } else {
+      ssim_zero_words_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(
+          static_cast<unsigned long long*>(ptr), (int)(kScratchBytes / 8));
+      s.status = hipGetLastError() == hipSuccess ? SSIM_OK : SSIM_ERR_HIP;
+      s.ptr = ptr;
+    }
+    s.ready = true;
+  }
+  *out = s.ptr;
+  return s.status;
+}
+
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -300,11 +351,15 @@ constexpr int kRecompRowsPerBlock = 8;
 
 // ref (optional, with loss): the cached statistics of img2 written by
 // ssim_reference_stats; then only grad_img1 is formed.
+// use_scratch (with loss, workspace NULL): the accumulator is this device's
+// copy of the library's scratch array, looked up after every argument check.
 int recompute_impl(const float* dloss, const void* img1, const void* img2, int dtype, int64_t N,
                    int64_t C, int64_t H, int64_t W, int padding, float* loss, void* workspace,
-                   void* grad_img1, void* grad_img2, void* stream, const float* ref = nullptr) {
+                   void* grad_img1, void* grad_img2, void* stream, const float* ref = nullptr,
+                   bool use_scratch = false) {
   if (!dloss || !img1 || !img2) return SSIM_ERR_NULL;
-  if (loss && !workspace) return SSIM_ERR_NULL;
+  if (use_scratch && (!loss || workspace)) return SSIM_ERR_NULL;
+  if (loss && !workspace && !use_scratch) return SSIM_ERR_NULL;
   Shape s;
   int rc = check_shape(N, C, H, W, padding, dtype, &s);
   if (rc != SSIM_OK) return rc;
@@ -329,6 +384,10 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   const DeviceInfo* d = nullptr;
   rc = device_info(&d);
   if (rc != SSIM_OK) return rc;
+  if (use_scratch) {
+    rc = scratch_for_device(stream, &workspace);
+    if (rc != SSIM_OK) return rc;
+  }
 
   Params p;
   memset(&p, 0, sizeof(p));
@@ -594,6 +653,7 @@ const char* ssim_strerror(int code) {
     case SSIM_ERR_HIP: return "a HIP runtime call failed";
     case SSIM_ERR_DEVICE: return "the current device is not a wave64 gfx950 GPU";
     case SSIM_ERR_DTYPE: return "dtype must be SSIM_DTYPE_F32 (0), SSIM_DTYPE_F16 (1) or SSIM_DTYPE_BF16 (2)";
+    case SSIM_ERR_SCRATCH: return "the call needs more scratch than the library's fixed device array holds";
     default: return "unknown error code";
   }
 }
@@ -660,6 +720,19 @@ int ssim_loss_and_grad(const void* img1, const void* img2, int dtype, int64_t N,
   if (!loss) return SSIM_ERR_NULL;
   return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, workspace, grad_img1,
                         grad_img2, stream);
+}
+
+size_t ssim_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int ssim_loss_and_grad_noalloc(const void* img1, const void* img2, int dtype, int64_t N,
+                               int64_t C, int64_t H, int64_t W, int padding, const float* dloss,
+                               float* loss, void* grad_img1, void* grad_img2, void* stream) {
+  if (!loss) return SSIM_ERR_NULL;
+  // every shape the step accepts needs one accumulator (a Workspace) of
+  // scratch, whatever its size; a larger need would be refused here
+  if (sizeof(Workspace) > kScratchBytes) return SSIM_ERR_SCRATCH;
+  return recompute_impl(dloss, img1, img2, dtype, N, C, H, W, padding, loss, nullptr, grad_img1,
+                        grad_img2, stream, nullptr, true);
 }
 
 int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n, void* stream) {

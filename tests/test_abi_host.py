@@ -43,7 +43,7 @@ def test_abi_version_and_strerror():
     hdr = open(HEADER).read()
     v = int(re.search(r"#define SSIM_ABI_VERSION (\d+)", hdr).group(1))
     assert S.ssim_abi_version() == v == S.ABI_VERSION
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert S.ssim_strerror(code)
     assert "unknown" in S.ssim_strerror(-99)
 
@@ -178,6 +178,26 @@ def test_loss_and_grad_argument_errors_return_before_any_hip_call():
     assert _lag(lib, loss=0x100000 + 16) == -5      # loss inside img2
     assert _lag(lib, ws=0x900000 + 4096) == -5      # workspace overlaps a gradient
     assert _lag(lib, loss=0x300000 + 8) == -5       # loss inside the workspace
+
+
+def test_noalloc_argument_errors_return_before_any_hip_call():
+    lib = S.lib()
+    f = lambda **kw: lib.ssim_loss_and_grad_noalloc(
+        kw.get("img1", 0x10000), 0x100000, kw.get("dt", 0), 1, 1, kw.get("H", 64), 64,
+        kw.get("pad", 0), kw.get("dloss", 0x1000), kw.get("loss", 0x2000), kw.get("g1", 0x900000),
+        kw.get("g2", 0xA00000), None)
+    assert S.ssim_noalloc_scratch_bytes() >= S.ssim_workspace_bytes()
+    assert f(loss=None) == -1
+    assert f(dloss=None) == -1
+    assert f(img1=None) == -1
+    assert f(dt=3) == -8
+    assert f(pad=2) == -3
+    assert f(H=10) == -2
+    assert f(img1=0x10002) == -2
+    assert f(loss=0x100000 + 16) == -5      # loss inside img2
+    assert f(g1=0xA00000 + 8) == -5         # gradients overlap
+    assert f(g2=0x10000 + 4096) == -5       # gradient inside img1
+    assert "scratch" in S.ssim_strerror(-9)
 
 
 def test_grad_scale_argument_errors_return_before_any_hip_call():
