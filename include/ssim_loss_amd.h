@@ -117,10 +117,13 @@ size_t ssim_workspace_bytes(void);
  *   loss        : device fp32 scalar (output)
  *   saved_maps  : NULL for inference (no gradient will be taken), else a
  *                 device buffer of ssim_saved_maps_bytes(...) bytes that
- *                 receives, at every map entry, the four blurred quantities
- *                 the kernels form -- B(x - 1/2), B(y - 1/2), B((x - y)^2)
- *                 and B((x - 1/2)(y - 1/2)) -- one map plane each;
- *                 ssim_backward forms the loss partials from them.
+ *                 receives the forward's state for ssim_backward.  Its
+ *                 contents are opaque: only ssim_backward reads them, and
+ *                 they change meaning between versions of this ABI.  (In this
+ *                 version: at every map entry the four blurred quantities the
+ *                 kernels form -- B(y), B(x - y), B((x - y)^2) and
+ *                 B((x - 1/2)(y - 1/2)) -- one map plane each; ssim_backward
+ *                 forms the loss partials from them.)
  *   workspace   : device buffer of ssim_workspace_bytes() bytes, zeroed
  *                 before its first use
  *   stream      : hipStream_t (NULL = default stream)
@@ -262,7 +265,7 @@ int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n
  * Cached reference statistics.  In a training run the second image is often
  * a fixed reference (the ground-truth view, with only the first image
  * differentiable: "Fully Fused Differentiable SSIM", Constraints).  Of the
- * statistics the kernels blur, B(y - 1/2) depends on the reference alone; it
+ * statistics the kernels blur, B(y) depends on the reference alone; it
  * can be computed once per reference and reused by every step that compares
  * against it.  (The pages' SSIMULACRA2 port caches reference-side work the
  * same way; here it is the one reference-only statistic of the SSIM basis.)
@@ -274,13 +277,13 @@ int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n
  * arguments.  Host-only. */
 size_t ssim_reference_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int padding);
 
-/* Writes B(img2 - 1/2) (the reference's blurred mean, shifted) to `ref`
+/* Writes B(img2) (the reference's blurred mean) to `ref`
  * (device, ssim_reference_bytes(...) bytes).  img2: device image of
  * `dtype`.  The result is valid for that exact image, shape and padding. */
 int ssim_reference_stats(const void* img2, int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
                          int padding, float* ref, void* stream);
 
-/* As ssim_loss_and_grad with grad_img2 = NULL, reading B(img2 - 1/2) from
+/* As ssim_loss_and_grad with grad_img2 = NULL, reading B(img2) from
  * `ref` (ssim_reference_stats of this img2) instead of forming it: loss =
  * 1 - mean SSIM and grad_img1 = *dloss * d loss / d img1 in one launch, one
  * blur fewer in each direction.  img2 is still read (the other statistics mix

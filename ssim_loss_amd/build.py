@@ -3,7 +3,13 @@ compiled in parallel with ``hipcc`` for gfx950 and linked into
 ``ssim_loss_amd/libssim_loss_amd.so``.
 
 Packed-FP32 instructions are switched off (``-packed-fp32-ops``); the kernels
-are written so that nothing depends on them.
+are written so that nothing depends on them.  Floating-point contraction is
+limited to single expressions (``-ffp-contract=on``, not HIP's default of
+fusing across statements): every fused multiply-add the arithmetic relies on
+is written out, and a product stored to a variable must stay rounded -- the
+forward's blurs by parts are exact on constant windows only if, say, a
+squared difference is rounded before the difference from its neighbour is
+taken.
 """
 from __future__ import annotations
 
@@ -32,8 +38,8 @@ def hipcc() -> str:
 
 
 def compile_flags(extra: list[str] | None = None) -> list[str]:
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE,
-            "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=on",
+            "-I", INCLUDE, "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             *(extra or [])]
 
 

@@ -606,7 +606,7 @@ int vol_backward_impl(const float* dloss, const void* img1, const void* img2, in
   return launch_vol(d, dtype, kKVolBwd, p, stream);
 }
 
-// The cached reference statistics of img2: B(img2 - 1/2) on the map, one
+// The cached reference statistics of img2: B(img2) on the map, one
 // fp32 plane per image plane with the saved-maps row pitch.
 int ref_stats_impl(const void* img2, int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
                    int padding, float* ref, void* stream) {

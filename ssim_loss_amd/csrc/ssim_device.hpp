@@ -14,21 +14,23 @@
 //   * One blur pass serves several statistics ("Fully Fused Differentiable
 //     SSIM", opening section).  SSIM needs the second moments only through
 //     sigma_xy and sigma_x^2 + sigma_y^2 = 2 sigma_xy + var(x - y), so four
-//     blurred quantities suffice: mu_x' = B(x'), mu_y' = B(y'),
-//     P' = B(x' y') and R = B((x - y)^2), with x' = x - 1/2, y' = y - 1/2.
-//     Then, with dmu = mu_x - mu_y,
+//     blurred quantities suffice: mu_y = B(y), mu_d = B(x - y),
+//     R = B((x - y)^2) and P' = B(x' y'), with x' = x - 1/2, y' = y - 1/2.
+//     Then mu_x = mu_y + mu_d, dmu = mu_d, mu' = mu - 1/2 and
 //         A1 = 2 mu_x mu_y + C1,  D1 = dmu^2,            B1 = A1 + D1
 //         A2 = 2 (P' - mu_x' mu_y') + C2,  D2 = R - dmu^2, B2 = A2 + D2
 //         1 - S = (A1 D2 + D1 B2) / (B1 B2).
-//     The shift by 1/2 leaves every variance unchanged and halves the
+//     The shift by 1/2 leaves every covariance unchanged and halves the
 //     magnitudes that cancel in P' - mu_x' mu_y'; the difference basis makes
 //     B1 - A1 and B2 - A2 exact by construction, so identical images give a
 //     loss and gradients of exactly zero and near-identical images (SSIM
 //     near 1, the end of a training run) keep full relative accuracy in
-//     1 - S, which is what the loss sums.
+//     1 - S, which is what the loss sums.  The forward blurs all four by
+//     parts (blur11_by_parts), which is exact on a constant window; why that
+//     matters is at ssim_terms.
 //   * The pages send five upstream gradients through B^T (mu1, mu2, s11, s22,
-//     s12); in the basis above there are four, m0..m3 = d loss /
-//     d(mu_x', mu_y', R, P') (R's with the chain rule's 2 folded in), and
+//     s12); here there are four, m0..m3 = d loss / d(mu_x, mu_y, R, P') (R's
+//     with the chain rule's 2 folded in), and
 //         grad_x = dloss * (B^T m0 + y' * B^T m3 + (x - y) * B^T m2)
 //         grad_y = dloss * (B^T m1 + x' * B^T m3 - (x - y) * B^T m2).
 //   * The window is symmetric and B^T of a zero-filled correlation is a
@@ -45,8 +47,10 @@
 //   column pass : lane t owns input column j0 - off + t.  It marches down the
 //                 rows, loading its own pixel per row straight from HBM
 //                 (coalesced across lanes), and keeps the last 11 rows of the
-//                 four quantities in a 12-slot register ring; each new row
-//                 gives one column-blurred row of the four quantities.
+//                 four quantities in a 12-slot register ring (the forward's
+//                 as differences from the row before, for the blur by
+//                 parts); each new row gives one column-blurred row of the
+//                 four quantities.
 //   row pass    : batches of 4 column-blurred rows go through a double-
 //                 buffered LDS tile [quantity][row][256] (32 KiB); wave w then
 //                 takes row w of the batch and lane l produces the 4 adjacent
@@ -124,6 +128,78 @@ __host__ __device__ constexpr float tap(int k) {
                              : kTap5;
 }
 
+// Partial sums of the taps, H_j = g_0 + ... + g_{j-1} for j = 1 .. 10, from
+// the fp64 Gaussian, rounded once to fp32.  By symmetry the tail sums
+// g_j + ... + g_10 are H_{11-j}.
+constexpr float kHead1 = 0.0010283800844791101f;
+constexpr float kHead2 = 0.0086271382197182951f;
+constexpr float kHead3 = 0.044627910348149127f;
+constexpr float kHead4 = 0.15398859985784913f;
+constexpr float kHead5 = 0.36699413756910282f;
+constexpr float kHead6 = 0.63300586243089718f;
+constexpr float kHead7 = 0.84601140014215082f;
+constexpr float kHead8 = 0.95537208965185094f;
+constexpr float kHead9 = 0.99137286178028172f;
+constexpr float kHead10 = 0.99897161991552086f;
+
+__host__ __device__ constexpr float head(int j) {
+  return j == 1 ? kHead1 : j == 2 ? kHead2 : j == 3 ? kHead3 : j == 4 ? kHead4
+       : j == 5 ? kHead5 : j == 6 ? kHead6 : j == 7 ? kHead7 : j == 8 ? kHead8
+       : j == 9 ? kHead9 : kHead10;
+}
+// tail sum g_j + ... + g_10, j = 1 .. 10
+__host__ __device__ constexpr float tail(int j) { return head(11 - j); }
+
+// The forward blurs some quantities by parts.  For a window w(0) .. w(10),
+//   sum_a g_a w(a) = w(10) - sum_{j=1}^{10} H_j (w(j) - w(j-1))
+// (the taps sum to 1), so the blur takes the window's newest value and its
+// ten differences.  A constant window has zero differences and comes out
+// exactly as its value, where the plain sum g_0 w(0) + g_1 w(1) + ... rounds
+// the partial sums; and each difference is formed once per input and shared
+// by every window that contains it.  See ssim_terms for why the forward needs
+// exact constant windows.
+template <typename D>
+__device__ __forceinline__ float blur11_by_parts(float newest, const D& dlt) {
+  float acc = newest;
+#pragma unroll
+  for (int j = 1; j < 11; ++j) acc = __builtin_fmaf(-head(j), dlt(j), acc);
+  return acc;
+}
+
+// The plain 11-tap blur of a window w(0) .. w(10): g_0 w(0), then ten fused
+// multiply-adds in tap order.
+template <typename W>
+__device__ __forceinline__ float blur11_plain(const W& w) {
+  float acc = tap(0) * w(0);
+#pragma unroll
+  for (int a = 1; a < 11; ++a) acc = __builtin_fmaf(tap(a), w(a), acc);
+  return acc;
+}
+
+// Four adjacent outputs of one row from the 14 inputs v[0] .. v[13] (output
+// u reads v[u] .. v[u + 10]), by parts (kParts: the 13 differences shared
+// by the four) or plain.
+template <bool kParts>
+__device__ __forceinline__ void blur4(const float (&v)[16], float (&o)[4]) {
+  if constexpr (kParts) {
+    // tap by tap across the four outputs (the order blur11_by_parts takes),
+    // so that each difference is formed once and only a few are live
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = v[u + 10];
+#pragma unroll
+    for (int j = 1; j < 11; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = __builtin_fmaf(-head(j), v[u + j] - v[u + j - 1], o[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = blur11_plain([&](int a) { return v[u + a]; });
+  }
+}
+
+// The forward's four quantities (y, x - y, (x - y)^2 and x' y') are blurred
+// by parts, the backward's partials plainly.
+constexpr int kByParts = 4;
+
 constexpr float kC1 = 1.0e-4f;  // (0.01 * 1)^2
 constexpr float kC2 = 9.0e-4f;  // (0.03 * 1)^2
 constexpr float kShift = 0.5f;  // x' = x - 1/2 (see the file header)
@@ -135,7 +211,7 @@ struct Workspace {
   unsigned long long pad[31];
 };
 
-// kRef: blur a reference image alone and store its blurred mean B(y - 1/2)
+// kRef: blur a reference image alone and store its blurred mean B(y)
 // (the statistic that depends on the reference only), for reuse across steps
 enum Mode { kFwdInfer = 0, kFwdTrain = 1, kBwd = 2, kRef = 3 };
 
@@ -295,22 +371,36 @@ __device__ __forceinline__ void st_img4(rsrc_t r, unsigned off, const float (&v)
 // SSIM at one map position
 
 // The SSIM terms at one map position, from the blurred quantities
-// mu_x', mu_y', R = B((x-y)^2), P' = B(x' y').
+// mu_y = B(y), mu_d = B(x - y), R = B((x - y)^2) and P' = B(x' y')
+// (x' = x - 1/2, y' = y - 1/2), with mu_x = mu_y + mu_d.  The first three are
+// blurred by parts, exact on constant windows:
+//   * a window on which y is constant gives mu_y = y, so mu_y' = mu_y - 1/2 is
+//     the very y' in P', and the covariance P' - mu_x' mu_y' carries no bias
+//     from a misrounded mean (an 8-bit flat region of a reference image, say:
+//     otherwise the same few-ulp error would enter every such window and,
+//     divided by C2 = 9e-4, bias the loss);
+//   * dmu = mu_d is blurred from the differences themselves, with no
+//     cancellation between two means where the images nearly agree;
+//   * where both images are constant, dmu is the d = x - y of R, so
+//     D2 = R - dmu^2 is exactly 0 (R holds the rounded d^2 and D1 the rounded
+//     dmu^2).
 struct SsimTerms {
-  float mux, muy, dm, a1, d1, b1, a2, d2, b2, inv;
+  float mux, muy, mxs, mys, dm, a1, d1, b1, a2, d2, b2, inv;
 };
 
-__device__ __forceinline__ SsimTerms ssim_terms(float mxs, float mys, float rr, float pp) {
+__device__ __forceinline__ SsimTerms ssim_terms(float muy, float mud, float rr, float pp) {
   SsimTerms t;
-  t.mux = mxs + kShift;
-  t.muy = mys + kShift;
-  t.dm = mxs - mys;
+  t.muy = muy;
+  t.dm = mud;
+  t.mux = muy + mud;
+  t.mxs = t.mux - kShift;
+  t.mys = muy - kShift;
   t.a1 = __builtin_fmaf(2.0f * t.mux, t.muy, kC1);
   t.d1 = t.dm * t.dm;
   t.b1 = t.a1 + t.d1;
-  const float cov = __builtin_fmaf(-mxs, mys, pp);
+  const float cov = __builtin_fmaf(-t.mxs, t.mys, pp);
   t.a2 = __builtin_fmaf(2.0f, cov, kC2);
-  t.d2 = __builtin_fmaf(-t.dm, t.dm, rr);
+  t.d2 = rr - t.d1;
   t.b2 = t.a2 + t.d2;
   t.inv = __builtin_amdgcn_rcpf(t.b1 * t.b2);
   return t;
@@ -321,23 +411,24 @@ __device__ __forceinline__ float one_minus_ssim(const SsimTerms& t) {
   return __builtin_fmaf(t.a1, t.d2, t.d1 * t.b2) * t.inv;
 }
 
-// The four loss partials at one map position (k_m2 = -2/M).  With
-// S = A1 A2 inv, inv = 1/(B1 B2), and every term a multiple of D1, D2 or dmu
-// (so all vanish when x = y):
-//   dS/dmu_x' = 2 inv (mu_y T1 - mu_y' T2 + T3)
-//   dS/dmu_y' = 2 inv (mu_x T1 - mu_x' T2 - T3)
-//   dS/dP'    = 2 inv T2,      dS/dR = -S / B2 = -S B1 inv
+// The four loss partials at one map position (k_m2 = -2/M), with respect to
+// mu_x, mu_y (dmu = mu_x - mu_y), R and P'.  With S = A1 A2 inv,
+// inv = 1/(B1 B2), and every term a multiple of D1, D2 or dmu (so all vanish
+// when x = y):
+//   dS/dmu_x = 2 inv (mu_y T1 - mu_y' T2 + T3)
+//   dS/dmu_y = 2 inv (mu_x T1 - mu_x' T2 - T3)
+//   dS/dP'   = 2 inv T2,      dS/dR = -S / B2 = -S B1 inv
 // where T1 = A2 D1 / B1, T2 = A1 D2 / B2, T3 = S (B1 - B2) dmu.
 // Maps (loss = mean of 1 - S over M entries, k = -(2/M) inv):
-//   m0 = -(1/M) dS/dmu_x' = k (mu_y T1 - mu_y' T2 + T3)
-//   m1 = -(1/M) dS/dmu_y' = k (mu_x T1 - mu_x' T2 - T3)
+//   m0 = -(1/M) dS/dmu_x = k (mu_y T1 - mu_y' T2 + T3)
+//   m1 = -(1/M) dS/dmu_y = k (mu_x T1 - mu_x' T2 - T3)
 //   m2 = -(2/M) dS/dR     = -k S B1   (the chain rule's 2 folded in)
 //   m3 = -(1/M) dS/dP'    = k T2
 // Every product carries k inv = k_m2 inv^2 =: a once, so with X = a A1,
 // Y = a A2: k T2 = X D2 B1, k T1 = Y D1 B2, k T3 = X A2 (B1 - B2) dmu and
 // k S B1 = X A2 B1.  A zero k_m2 gives four zero partials.
-__device__ __forceinline__ void loss_partials(float mxs, float mys, const SsimTerms& t, float k_m2,
-                                              float (&m)[4]) {
+__device__ __forceinline__ void loss_partials(const SsimTerms& t, float k_m2, float (&m)[4]) {
+  const float mxs = t.mxs, mys = t.mys;
   const float a = k_m2 * t.inv * t.inv;
   const float X = a * t.a1, Y = a * t.a2;
   const float xa2 = X * t.a2;
@@ -389,7 +480,7 @@ __device__ __forceinline__ void load_row(const Params& p, const Seg<MODE>& s, in
   out.in = (s.colbyte != kOob) && ((unsigned)r < (unsigned)p.in_h);
 }
 
-// Quantities blurred by the forward: x', y', (x - y)^2 and x' y' with
+// Quantities blurred by the forward: y, x - y, (x - y)^2 and x' y' with
 // x' = x - 1/2, y' = y - 1/2.  Quantities blurred by the backward: the four
 // loss partials at each map entry, formed from the saved blurred quantities.
 template <int MODE>
@@ -398,17 +489,16 @@ __device__ __forceinline__ void quantities(const Raw<MODE>& r, float k_m2, float
     // the loss partials at this map entry; zero outside the map (the
     // adjoint's zero fill)
     float m[4];
-    loss_partials(r.v[0], r.v[1], ssim_terms(r.v[0], r.v[1], r.v[2], r.v[3]), k_m2, m);
+    loss_partials(ssim_terms(r.v[0], r.v[1], r.v[2], r.v[3]), k_m2, m);
 #pragma unroll
     for (int k = 0; k < 4; ++k) q[k] = r.in ? m[k] : 0.0f;
   } else {
     (void)k_m2;
-    const float x = r.v[0] - kShift, y = r.v[1] - kShift;
     const float d = r.v[0] - r.v[1];
-    q[0] = x;
-    q[1] = y;
+    q[0] = r.v[1];
+    q[1] = d;
     q[2] = d * d;
-    q[3] = x * y;
+    q[3] = (r.v[0] - kShift) * (r.v[1] - kShift);
   }
 }
 
@@ -460,7 +550,7 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
     // the reference's blurred mean, 16 contiguous bytes of its map row
     (void)dl;
     (void)acc;
-    st4<kNt>(s.out[0], g.base, make_float4(o[1][0], o[1][1], o[1][2], o[1][3]));
+    st4<kNt>(s.out[0], g.base, make_float4(o[0][0], o[0][1], o[0][2], o[0][3]));
   } else if constexpr (MODE != kBwd) {
     float s4 = 0.0f;
 #pragma unroll
@@ -483,7 +573,7 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
     float g1[4], g2[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      // chain rule: d mu_x'/dx = B^T, d P'/dx = y' B^T, d R/dx = 2 (x - y) B^T
+      // chain rule: d mu_x/dx = B^T, d P'/dx = y' B^T, d R/dx = 2 (x - y) B^T
       const float xs = g.xv[t] - kShift, ys = g.yv[t] - kShift, d = g.xv[t] - g.yv[t];
       g1[t] = dl * __builtin_fmaf(d, o[2][t], __builtin_fmaf(ys, o[3][t], o[0][t]));
       g2[t] = dl * __builtin_fmaf(-d, o[2][t], __builtin_fmaf(xs, o[3][t], o[1][t]));
@@ -511,8 +601,9 @@ __device__ __forceinline__ void consume(const Params& p, const Seg<MODE>& s,
 template <int MODE, bool kVec, bool kNt, int T, int PH>
 __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
                                       float (&tile)[2][kQ][kRows][kTileW],
-                                      float (&ring)[kRing][kQ], Raw<MODE> (&pre)[kRows], int t,
-                                      int buf, float dl, double& acc) {
+                                      float (&ring)[kRing][kQ], float (&prev)[kByParts],
+                                      Raw<MODE> (&pre)[kRows], int t, int buf, float dl,
+                                      double& acc) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -528,20 +619,26 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
 #pragma unroll
   for (int m = 0; m < kRows; ++m) load_row<MODE, T>(p, s, s.r0 + 10 + 4 * (t + 1) + m, pre[m]);
 
-  // column pass
+  // column pass.  The ring holds the backward's partials, and the forward's
+  // quantity 3, as values; the forward's quantities 0 .. 2 as differences
+  // from the row before (prev: that row's values), blurred by parts.
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
     const int base = 4 * PH + m;  // compile-time after unrolling
-    quantities<MODE>(cur[m], p.k_m2, ring[(base + 10) % kRing]);
-    float cs[kQ];
+    float nq[kQ];
+    quantities<MODE>(cur[m], p.k_m2, nq);
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) cs[q] = tap(0) * ring[base % kRing][q];
-#pragma unroll
-    for (int a = 1; a < 11; ++a)
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) cs[q] = __builtin_fmaf(tap(a), ring[(base + a) % kRing][q], cs[q]);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) tile[buf][q][m][tid] = cs[q];
+    for (int q = 0; q < kQ; ++q) {
+      if (MODE != kBwd && q < kByParts) {
+        ring[(base + 10) % kRing][q] = nq[q] - prev[q];
+        prev[q] = nq[q];
+        tile[buf][q][m][tid] =
+            blur11_by_parts(nq[q], [&](int j) { return ring[(base + j) % kRing][q]; });
+      } else {
+        ring[(base + 10) % kRing][q] = nq[q];
+        tile[buf][q][m][tid] = blur11_plain([&](int a) { return ring[(base + a) % kRing][q]; });
+      }
+    }
   }
   __syncthreads();
 
@@ -561,13 +658,8 @@ __device__ __forceinline__ void batch(const Params& p, const Seg<MODE>& s,
       v[4 * k + 2] = f.z;
       v[4 * k + 3] = f.w;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float a = tap(0) * v[u];
-#pragma unroll
-      for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
-      o[q][u] = a;
-    }
+    if (MODE != kBwd && q < kByParts) blur4<true>(v, o[q]);
+    else blur4<false>(v, o[q]);
   }
   consume<MODE, kVec, kNt, T>(p, s, g, o, dl, acc);
 }
@@ -718,24 +810,39 @@ __device__ __forceinline__ void strip_body(const Params& p) {
     const int nb = (s.nrows + kRows - 1) / kRows;
 
     float ring[kRing][kQ];
+    float prev[kByParts];
     Raw<MODE> warm[10];
     Raw<MODE> pre[kRows];
 #pragma unroll
     for (int k = 0; k < 10; ++k) load_row<MODE, T>(p, s, s.r0 + k, warm[k]);
 #pragma unroll
     for (int m = 0; m < kRows; ++m) load_row<MODE, T>(p, s, s.r0 + 10 + m, pre[m]);
+    // the first 10 rows of the window; for the quantities blurred by parts,
+    // each row's difference from the one before (slot 0's is never read)
 #pragma unroll
-    for (int k = 0; k < 10; ++k) quantities<MODE>(warm[k], p.k_m2, ring[k]);
+    for (int k = 0; k < 10; ++k) {
+      float nq[kQ];
+      quantities<MODE>(warm[k], p.k_m2, nq);
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (MODE != kBwd && q < kByParts) {
+          ring[k][q] = k > 0 ? nq[q] - prev[q] : 0.0f;
+          prev[q] = nq[q];
+        } else {
+          ring[k][q] = nq[q];
+        }
+      }
+    }
 
     for (int t = 0;;) {
       if (t >= nb) break;
-      batch<MODE, kVec, kNt, T, 0>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 0>(p, s, tile, ring, prev, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, kNt, T, 1>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 1>(p, s, tile, ring, prev, pre, t, buf, dl, acc);
       buf ^= 1;
       if (++t >= nb) break;
-      batch<MODE, kVec, kNt, T, 2>(p, s, tile, ring, pre, t, buf, dl, acc);
+      batch<MODE, kVec, kNt, T, 2>(p, s, tile, ring, prev, pre, t, buf, dl, acc);
       buf ^= 1;
       ++t;
     }

@@ -82,7 +82,7 @@ struct FSeg {
   bool last;            // the last strip: it owns the map columns right of its own range
   int i0;               // map row completed by the first batch row: u0 - off2
   int own_r1;           // the loss counts map rows [i0, own_r1)
-  rsrc_t ref;           // cached reference statistics: B(y - 1/2) map planes from p0
+  rsrc_t ref;           // cached reference statistics: B(y) map planes from p0
   unsigned ref_row;     // their row pitch, bytes
   unsigned ref_plane;   // their plane, bytes
 };
@@ -127,33 +127,55 @@ __device__ __forceinline__ void fload_row(const FSeg& s, int r, float (&v)[2]) {
   v[1] = ld_img<T>(s.img[1], off);
 }
 
+// The quantities the forward blurs: y, x - y, (x - y)^2 and x' y'
+// (x' = x - 1/2, y' = y - 1/2).
 __device__ __forceinline__ void image_quantities(const float (&v)[2], float (&q)[kQ]) {
-  const float x = v[0] - kShift, y = v[1] - kShift;
   const float d = v[0] - v[1];
-  q[0] = x;
-  q[1] = y;
+  q[0] = v[1];
+  q[1] = d;
   q[2] = d * d;
-  q[3] = x * y;
+  q[3] = (v[0] - kShift) * (v[1] - kShift);
 }
 
-// column pass of one row through a 12-slot ring: the new row goes into slot
-// (base + 10) % 12, and the output is the 11-tap sum over slots base..base+10.
-// Quantity kSkip (if any) is not blurred.
+// Stage 1's column pass of one image row through a 12-slot ring: the row's
+// quantities nq go into slot (base + 10) % 12 and the output is the 11-tap
+// blur over slots base .. base + 10.  Quantities 0 .. kByParts - 1 are kept
+// as differences from the row before (prev: that row's values) and blurred
+// by parts; quantity kSkip (if any) is not blurred.
+template <int kBase, int kSkip>
+__device__ __forceinline__ void ring_column_fwd(float (&ring)[kRing][kQ],
+                                                float (&prev)[kByParts], const float (&nq)[kQ],
+                                                float (&cs)[kQ]) {
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    if (q == kSkip) {
+      cs[q] = 0.0f;
+    } else if (q < kByParts) {
+      ring[(kBase + 10) % kRing][q] = nq[q] - prev[q];
+      prev[q] = nq[q];
+      cs[q] = blur11_by_parts(nq[q], [&](int j) { return ring[(kBase + j) % kRing][q]; });
+    } else {
+      ring[(kBase + 10) % kRing][q] = nq[q];
+      cs[q] = blur11_plain([&](int a) { return ring[(kBase + a) % kRing][q]; });
+    }
+  }
+}
+
+// Stage 2's column pass (the adjoint's, over the partials already in the
+// ring): plain 11-tap blurs over slots base .. base + 10.  Quantity kSkip
+// (if any) is not blurred.
 template <int kBase, int kSkip = -1>
 __device__ __forceinline__ void ring_column(float (&ring)[kRing][kQ], float (&cs)[kQ]) {
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) cs[q] = q == kSkip ? 0.0f : tap(0) * ring[kBase % kRing][q];
-#pragma unroll
-  for (int a = 1; a < 11; ++a)
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      if (q != kSkip) cs[q] = __builtin_fmaf(tap(a), ring[(kBase + a) % kRing][q], cs[q]);
+  for (int q = 0; q < kQ; ++q)
+    cs[q] = q == kSkip ? 0.0f : blur11_plain([&](int a) { return ring[(kBase + a) % kRing][q]; });
 }
 
 // row pass: 4 adjacent outputs of each of the 4 quantities from 16 columns of
 // a tile row starting at column c (16-byte aligned); quantity kSkip (if any)
-// is left alone
-template <int kSkip = -1>
+// is left alone.  kFwd: stage 1's image quantities (0 .. kByParts - 1 by
+// parts); otherwise plain.
+template <int kSkip = -1, bool kFwd = false>
 __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ][4]) {
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -168,13 +190,8 @@ __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ
       v[4 * k + 2] = f.z;
       v[4 * k + 3] = f.w;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float a = tap(0) * v[u];
-#pragma unroll
-      for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
-      o[q][u] = a;
-    }
+    if (kFwd && q < kByParts) blur4<true>(v, o[q]);
+    else blur4<false>(v, o[q]);
   }
 }
 
@@ -185,10 +202,13 @@ template <bool kLoss, int T, int PH, bool kRef>
 __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              float (&xyr)[kXYRing][2][kFTileW],
-                                             float (&ring)[kRing][kQ], float (&pre)[kRows][2],
-                                             unsigned mk, int t, int buf, int col, int wave,
-                                             int lane, double& acc) {
-  constexpr int kSkip = kRef ? 1 : -1;  // with a cached reference, B(y') is read, not blurred
+                                             float (&ring)[kRing][kQ], float (&prev)[kByParts],
+                                             float (&pre)[kRows][2], unsigned mk, int t, int buf,
+                                             int col, int wave, int lane, double& acc) {
+  // with a cached reference, B(y) (quantity 0) is read, not blurred, and the
+  // partial for mu_y (1), which feeds grad_y alone, is not passed on
+  constexpr int kSkip = kRef ? 0 : -1;
+  constexpr int kSkipPart = kRef ? 1 : -1;
   const int i = s.i0 + 4 * t + wave;
   const bool irow = (unsigned)i < (unsigned)p.map_h;
   const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
@@ -213,13 +233,13 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
 #pragma unroll
   for (int m = 0; m < kRows; ++m) {
     constexpr int kB0 = 4 * PH;
-    float cs[kQ];
-    image_quantities(cur[m], ring[(kB0 + m + 10) % kRing]);
+    float cs[kQ], nq[kQ];
+    image_quantities(cur[m], nq);
     switch (m) {  // m is a compile-time constant after unrolling
-      case 0: ring_column<kB0 + 0, kSkip>(ring, cs); break;
-      case 1: ring_column<kB0 + 1, kSkip>(ring, cs); break;
-      case 2: ring_column<kB0 + 2, kSkip>(ring, cs); break;
-      default: ring_column<kB0 + 3, kSkip>(ring, cs); break;
+      case 0: ring_column_fwd<kB0 + 0, kSkip>(ring, prev, nq, cs); break;
+      case 1: ring_column_fwd<kB0 + 1, kSkip>(ring, prev, nq, cs); break;
+      case 2: ring_column_fwd<kB0 + 2, kSkip>(ring, prev, nq, cs); break;
+      default: ring_column_fwd<kB0 + 3, kSkip>(ring, prev, nq, cs); break;
     }
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
@@ -231,7 +251,7 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
   // jm0 + 4l .. 4l+3.  The partials go back into the row just read.
   float muy_ref[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (kRef) {
-    // the cached B(y - 1/2) at this lane's 4 map entries (0 outside the map)
+    // the cached B(y) at this lane's 4 map entries (0 outside the map)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const unsigned cb = plane_col(p, s, s.rv0 - p.off2 + 4 * lr + c, p.map_w, s.ref_plane, 4u);
@@ -241,10 +261,10 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
   float part[kQ][4];
   if (irow) {
     float o[kQ][4];
-    row_pass<kSkip>(&tile[buf][0][wave][0], 4 * lr, o);
+    row_pass<kSkip, true>(&tile[buf][0][wave][0], 4 * lr, o);
     if constexpr (kRef) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[1][c] = muy_ref[c];
+      for (int c = 0; c < 4; ++c) o[0][c] = muy_ref[c];
     }
     const bool own_row = kLoss && i < s.own_r1;
     float s4 = 0.0f;
@@ -255,7 +275,7 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
       float m4[4];
       // outside the map the partials are the adjoint's zero fill (a zero
       // scale: every input of the row pass is finite, the overhang included)
-      loss_partials(o[0][c], o[1][c], st, in_map ? p.k_m2 : 0.0f, m4);
+      loss_partials(st, in_map ? p.k_m2 : 0.0f, m4);
 #pragma unroll
       for (int k = 0; k < kQ; ++k) part[k][c] = m4[k];
       if constexpr (kLoss) {
@@ -273,7 +293,7 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
   if (lane < kFMapLanes) {
 #pragma unroll
     for (int k = 0; k < kQ; ++k)
-      if (k != kSkip)
+      if (k != kSkipPart)
         *reinterpret_cast<float4*>(&tile[buf][k][wave][4 * lane]) =
             make_float4(part[k][0], part[k][1], part[k][2], part[k][3]);
   }
@@ -444,7 +464,7 @@ __device__ __forceinline__ int segment_batches(const FSeg& s) {
 // batches before it in this workgroup) mod 2; per segment each group passes
 // 2 (nb + 1) barriers (stage 2 idles through the first tick, stage 1
 // through the last), so the two loops meet at every barrier.
-// kRef: B(y - 1/2) comes from a cached map (p.maps, the layout the
+// kRef: B(y) comes from a cached map (p.maps, the layout the
 // reference-statistics kernel writes) and only grad_x is formed.
 template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false>
 __device__ __forceinline__ void fused_body(const Params& p) {
@@ -475,6 +495,7 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       const int nb = segment_batches(s);
       const unsigned mk = fused_masks(p, s, lane);
       float ring[kRing][kQ];
+      float prev[kByParts];
       float pre[kRows][2];
       {
         float warm[10][2];
@@ -482,20 +503,35 @@ __device__ __forceinline__ void fused_body(const Params& p) {
         for (int k = 0; k < 10; ++k) fload_row<T>(s, s.u0 - 10 + k, warm[k]);
 #pragma unroll
         for (int m = 0; m < kRows; ++m) fload_row<T>(s, s.u0 + m, pre[m]);
+        // the first 10 rows of the window; for the quantities blurred by
+        // parts, each row's difference from the one before (slot 0's is
+        // never read)
 #pragma unroll
-        for (int k = 0; k < 10; ++k) image_quantities(warm[k], ring[k]);
+        for (int k = 0; k < 10; ++k) {
+          float nq[kQ];
+          image_quantities(warm[k], nq);
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            if (q < kByParts) {
+              ring[k][q] = k > 0 ? nq[q] - prev[q] : 0.0f;
+              prev[q] = nq[q];
+            } else {
+              ring[k][q] = nq[q];
+            }
+          }
+        }
       }
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         ++t;

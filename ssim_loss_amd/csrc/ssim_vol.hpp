@@ -162,11 +162,11 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
         for (int q = 0; q < kQ; ++q) A[q][r][c] = pre.v[it][q];
       } else {
         const float xv = pre.v[it][0], yv = pre.v[it][1];
-        const float xs = xv - kShift, ys = yv - kShift, d = xv - yv;
-        A[0][r][c] = xs;
-        A[1][r][c] = ys;
+        const float d = xv - yv;
+        A[0][r][c] = yv;
+        A[1][r][c] = d;
         A[2][r][c] = d * d;
-        A[3][r][c] = xs * ys;
+        A[3][r][c] = (xv - kShift) * (yv - kShift);
       }
     }
   }
@@ -178,7 +178,10 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
 // as four 16-byte words; consecutive lanes take consecutive rows, so with
 // the 28-float row pitch any 8 (or 16) of them read distinct bank groups,
 // and their 4 single-word stores land on consecutive words.
+// kFwd: the forward's quantities, blurred by parts in every pass (all four
+// here, so that no wave splits between the two forms); otherwise plain.
 constexpr int kXTasks = kQ * (kVT / 4) * kVInY;
+template <bool kFwd>
 __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
                                           float (&Bx)[kQ][kVT][kVByP]) {
 #pragma unroll
@@ -199,13 +202,7 @@ __device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
         v[4 * k + 3] = f.w;
       }
       float o[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float a = tap(0) * v[u];
-#pragma unroll
-        for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
-        o[u] = a;
-      }
+      blur4<kFwd>(v, o);
 #pragma unroll
       for (int u = 0; u < 4; ++u) Bx[q][4 * g + u][r] = o[u];
     }
@@ -224,6 +221,7 @@ __device__ __forceinline__ int vol_crow(int r) { return r ^ ((r >> 2) & 1); }
 // unused): 4 reads per 4 outputs instead of 44.  Consecutive lanes take
 // consecutive columns, whose 44-word pitch puts any 8 of them on distinct
 // bank quads.  The outputs go to the transpose tile C[q][row][column].
+template <bool kFwd>
 __device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
                                           float (&C)[kQ][kVTy][kVT]) {
   const int t = threadIdx.x;
@@ -238,13 +236,10 @@ __device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
     v[4 * k + 2] = f.z;
     v[4 * k + 3] = f.w;
   }
+  float o[4];
+  blur4<kFwd>(v, o);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float a = tap(0) * v[u];
-#pragma unroll
-    for (int b = 1; b < 11; ++b) a = __builtin_fmaf(tap(b), v[u + b], a);
-    C[q][vol_crow(4 * g + u)][tx] = a;
-  }
+  for (int u = 0; u < 4; ++u) C[q][vol_crow(4 * g + u)][tx] = o[u];
 }
 
 // The four XY-blurred quantities at this lane's (i, j), from the transpose
@@ -303,6 +298,72 @@ __device__ __forceinline__ void vol_zpass(float (&acc)[11][kQ], const float (&a)
     acc[0][q] = tap(0) * a[q];
   }
 }
+
+// The forward's Z pass, by parts: the output whose window has slices
+// z0 .. z0 + 10 is v(z0) + sum_{j=1}^{10} T_j (v(z0 + j) - v(z0 + j - 1)),
+// T_j = g_j + ... + g_10 (the taps sum to 1), exact for a window that is
+// constant along depth.  acc[c] holds that sum for the window whose oldest
+// slice arrived c slices ago, with its first c differences in; a new value a
+// with difference dl = a - prev (prev: the value before it) moves every sum
+// one difference on, acc[c] <- acc[c - 1] + T_c dl, and starts the newest,
+// acc[1] = prev + T_1 dl, in descending c as above.  acc[10] is then the
+// complete sum of the window that ends at the new slice.
+#define SSIM_TAIL1_BITS 0x3f7fbc9b
+#define SSIM_TAIL2_BITS 0x3f7dca9d
+#define SSIM_TAIL3_BITS 0x3f749344
+#define SSIM_TAIL4_BITS 0x3f589434
+#define SSIM_TAIL5_BITS 0x3f220cac
+#define SSIM_TAIL6_BITS 0x3ebbe6a8
+#define SSIM_TAIL7_BITS 0x3e1daf30
+#define SSIM_TAIL8_BITS 0x3d36cbc1
+#define SSIM_TAIL9_BITS 0x3c0d58d7
+#define SSIM_TAIL10_BITS 0x3a86cab6
+static_assert(__builtin_bit_cast(unsigned, tail(1)) == SSIM_TAIL1_BITS &&
+                  __builtin_bit_cast(unsigned, tail(2)) == SSIM_TAIL2_BITS &&
+                  __builtin_bit_cast(unsigned, tail(3)) == SSIM_TAIL3_BITS &&
+                  __builtin_bit_cast(unsigned, tail(4)) == SSIM_TAIL4_BITS &&
+                  __builtin_bit_cast(unsigned, tail(5)) == SSIM_TAIL5_BITS &&
+                  __builtin_bit_cast(unsigned, tail(6)) == SSIM_TAIL6_BITS &&
+                  __builtin_bit_cast(unsigned, tail(7)) == SSIM_TAIL7_BITS &&
+                  __builtin_bit_cast(unsigned, tail(8)) == SSIM_TAIL8_BITS &&
+                  __builtin_bit_cast(unsigned, tail(9)) == SSIM_TAIL9_BITS &&
+                  __builtin_bit_cast(unsigned, tail(10)) == SSIM_TAIL10_BITS,
+              "the by-parts Z pass's literals are the tail sums' fp32 bits");
+#define SSIM_ZPART(c, BITS)                                                  \
+  asm("v_fmamk_f32 %0, %1, " SSIM_STR(BITS) ", %2"                           \
+      : "=v"(acc[c][q])                                                      \
+      : "v"(dl), "v"(acc[c - 1][q]))
+__device__ __forceinline__ void vol_zpass_by_parts(float (&acc)[11][kQ], const float (&a)[kQ],
+                                                   float (&prev)[kQ]) {
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const float dl = a[q] - prev[q];
+    SSIM_ZPART(10, SSIM_TAIL10_BITS);
+    SSIM_ZPART(9, SSIM_TAIL9_BITS);
+    SSIM_ZPART(8, SSIM_TAIL8_BITS);
+    SSIM_ZPART(7, SSIM_TAIL7_BITS);
+    SSIM_ZPART(6, SSIM_TAIL6_BITS);
+    SSIM_ZPART(5, SSIM_TAIL5_BITS);
+    SSIM_ZPART(4, SSIM_TAIL4_BITS);
+    SSIM_ZPART(3, SSIM_TAIL3_BITS);
+    SSIM_ZPART(2, SSIM_TAIL2_BITS);
+    asm("v_fmamk_f32 %0, %1, " SSIM_STR(SSIM_TAIL1_BITS) ", %2"
+        : "=v"(acc[1][q])
+        : "v"(dl), "v"(prev[q]));
+    prev[q] = a[q];
+  }
+}
+#undef SSIM_ZPART
+#undef SSIM_TAIL1_BITS
+#undef SSIM_TAIL2_BITS
+#undef SSIM_TAIL3_BITS
+#undef SSIM_TAIL4_BITS
+#undef SSIM_TAIL5_BITS
+#undef SSIM_TAIL6_BITS
+#undef SSIM_TAIL7_BITS
+#undef SSIM_TAIL8_BITS
+#undef SSIM_TAIL9_BITS
+#undef SSIM_TAIL10_BITS
 #undef SSIM_ZMOVE
 #undef SSIM_STR
 #undef SSIM_STR_
@@ -360,7 +421,7 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
     acc += off != kOob ? (double)one_minus_ssim(st) : 0.0;
     if constexpr (MODE == kFwdTrain) {
       float m[4];
-      loss_partials(o[0], o[1], st, p.k_m2, m);
+      loss_partials(st, p.k_m2, m);
 #pragma unroll
       for (int q = 0; q < kQ; ++q) st1<kNt>(s.out[q], off, m[q]);
     }
@@ -417,6 +478,7 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     // C[(j - 1) & 1] into the Z sums.  No buffer is written in the step that
     // reads its other use, and each stage reads what an earlier step wrote.
     float acc_z[11][kQ];
+    float zprev[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};  // the forward's by-parts Z pass
 #pragma unroll
     for (int k = 0; k < 11; ++k)
 #pragma unroll
@@ -434,13 +496,14 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
         vol_store<MODE>(pre, A[j & 1]);
         vol_load<MODE, T>(p, s, kin0 + j + 1, eo, pre);
       }
-      if (j >= 1 && j <= nsl) vol_xpass(A[(j - 1) & 1], Bx[(j - 1) & 1]);
-      if (j >= 2 && j <= nsl + 1) vol_ypass(Bx[j & 1], C[j & 1]);
+      if (j >= 1 && j <= nsl) vol_xpass<MODE != kBwd>(A[(j - 1) & 1], Bx[(j - 1) & 1]);
+      if (j >= 2 && j <= nsl + 1) vol_ypass<MODE != kBwd>(Bx[j & 1], C[j & 1]);
       // (before slice 0 reaches the Z pass the sums take zeros, which leave
       // them unchanged but keep their update out of any branch)
       float a[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (j >= 3) vol_ytake(C[(j - 1) & 1], a);
-      vol_zpass(acc_z, a);
+      if constexpr (MODE == kBwd) vol_zpass(acc_z, a);
+      else vol_zpass_by_parts(acc_z, a, zprev);
       const int n = j - 13;  // output slice k0 + n, once its 11 slices are in
       if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, oo, acc_z[10], xy, dl, acc);
       // the chain rule's x, y for the next step's output slice

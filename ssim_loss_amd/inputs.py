@@ -81,14 +81,43 @@ def smooth_field(rng: np.random.Generator, C: int, H: int, W: int, components: i
     return out
 
 
+# Flat levels of the "objects" and "flat" kinds: dark and bright values whose
+# offset from 1/2 is not exact in fp32 arithmetic, two 8-bit codes, and
+# mid-grey ones.
+FLAT_LEVELS = (0.05, 13 / 255, 0.3, 0.7, 242 / 255, 0.95)
+
+
+def flat_objects(rng: np.random.Generator, C: int, H: int, W: int, count: int = 6) -> np.ndarray:
+    """A black background with `count` axis-aligned flat rectangles per
+    channel, each at a level drawn from FLAT_LEVELS (later ones cover earlier
+    ones).  fp64."""
+    out = np.zeros((C, H, W), np.float64)
+    for c in range(C):
+        for _ in range(count):
+            h = int(rng.integers(max(1, H // 8), max(2, H // 2)))
+            w = int(rng.integers(max(1, W // 8), max(2, W // 2)))
+            i = int(rng.integers(0, H - h + 1))
+            j = int(rng.integers(0, W - w + 1))
+            out[c, i:i + h, j:j + w] = FLAT_LEVELS[int(rng.integers(len(FLAT_LEVELS)))]
+    return out
+
+
 def _one_image(rng: np.random.Generator, C: int, H: int, W: int, kind: str,
                noise: float) -> tuple[np.ndarray, np.ndarray]:
+    """kinds: "uniform" U[0,1); "field" the smooth field; "constant" one
+    value; "objects" flat rectangles on black (flat_objects); "dark-field" a
+    low-contrast dark field, 0.02 + 0.04 * smooth field.
+    img2 = clamp(img1 + N(0, noise^2))."""
     if kind == "uniform":
         a = rng.random((C, H, W))
     elif kind == "field":
         a = smooth_field(rng, C, H, W)
     elif kind == "constant":
         a = np.full((C, H, W), rng.random())
+    elif kind == "objects":
+        a = flat_objects(rng, C, H, W)
+    elif kind == "dark-field":
+        a = 0.02 + 0.04 * smooth_field(rng, C, H, W, texture=0.0)
     else:
         raise ValueError(f"unknown kind {kind!r}")
     b = np.clip(a + rng.normal(0.0, noise, a.shape), 0.0, 1.0) if noise > 0 else a.copy()
@@ -123,6 +152,15 @@ def make_pair(shape, kind: str = "uniform", noise: float = 0.05, seed: int = 0,
     x = np.stack([p[0] for p in pairs])
     y = np.stack([p[1] for p in pairs])
     return np.ascontiguousarray(x), np.ascontiguousarray(y)
+
+
+def flat_pair(shape, level: float, noise: float, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """img1 = `level` everywhere, img2 = clamp(img1 + N(0, noise^2)), fp32,
+    any rank (a render that is flat where the other image has texture)."""
+    rng = np.random.default_rng(seed)
+    a = np.full(shape, float(level))
+    b = np.clip(a + rng.normal(0.0, noise, a.shape), 0.0, 1.0)
+    return np.ascontiguousarray(a.astype(np.float32)), np.ascontiguousarray(b.astype(np.float32))
 
 
 def make_workload(name: str) -> tuple[np.ndarray, np.ndarray]:

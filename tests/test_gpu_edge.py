@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from ssim_loss_amd.inputs import make_pair
+from ssim_loss_amd.inputs import FLAT_LEVELS, flat_pair, make_pair
 
 from gpu_util import GRAD_RTOL, check_grad, check_loss, gpu_run, say
 
@@ -83,36 +83,46 @@ def test_identical_images_give_exact_zero(padding):
         assert gl == 0.0 and not g1.any() and not g2.any()
 
 
-def _constant_bound(a, b):
-    """fp32 error model for constant images.  Their variances vanish, so
-    B2 = C2 + (rounding residue of R - dmu^2 and of P' - mu_x' mu_y'), a few
-    ulps of (a - b)^2 and |(a - 1/2)(b - 1/2)|; S, 1 - S and every partial
-    then carry that residue relative to C2 = 9e-4."""
-    return 64 * 2.0 ** -24 * ((a - b) ** 2 + 2 * abs((a - 0.5) * (b - 0.5))) / 9e-4
+def constant_grad_bar(a, b):
+    """The gradient bar for images constant at levels a and b: the contract's
+    1e-4 of the largest gradient, or the fp32 error of the chain rule's
+    cancellation if that is larger.  With zero variance and different means,
+    the mean path (B^T of the mu_x partial) and the second-moment path
+    ((x - y) B^T of the R partial) each carry about S B1 / B2 times the
+    gradient they add up to (B1 = a^2 + b^2 + C1, B2 = C2), so their fp32
+    rounding, a few units of 2^-24 of each, shows at 2^-24 B1 / C2 of the
+    result; 32 units of that bound it.  Every separable adjoint in fp32 has
+    this cancellation; the loss itself keeps the contract's bar."""
+    b1 = a * a + b * b + 1e-4
+    return max(GRAD_RTOL, 32 * 2.0 ** -24 * b1 / 9e-4)
 
 
 @pytest.mark.parametrize("padding", ["valid", "same"])
-@pytest.mark.parametrize("a,b", [(0.25, 0.75), (0.0, 1.0), (0.9, 0.1), (0.5, 0.5)])
+@pytest.mark.parametrize("a,b", [(0.25, 0.75), (0.0, 1.0), (0.9, 0.1), (0.5, 0.5), (0.05, 0.95),
+                                 (0.3, 0.31), (13 / 255, 14 / 255), (1.0, 0.98)])
 def test_constant_images(a, b, padding):
-    """Constant images against the oracle, within the fp32 error model above;
-    in valid padding also against S = (2ab + C1)/(a^2 + b^2 + C1)."""
+    """Constant images against the oracle: the loss at the contract's bar (and
+    in valid padding against S = (2ab + C1)/(a^2 + b^2 + C1)), the gradients
+    at constant_grad_bar.  The variances vanish, so a rounding bias in a
+    blurred mean or in B((x - y)^2) would be divided by C2 = 9e-4: the
+    forward blurs by parts, which gives a constant window's value exactly."""
     say(f"[stability] constant {a} {b} {padding}")
     x = np.full((1, 2, 40, 50), a, np.float32)
     y = np.full((1, 2, 40, 50), b, np.float32)
-    bound = _constant_bound(a, b)
     gl, g1, g2 = gpu_run(x, y, padding)
     if a == b:  # identical images: exactly zero (the oracle shows fp64 noise here)
         assert gl == 0.0 and not g1.any() and not g2.any()
         return
     ol, o1, o2 = oracle.ssim_loss(x, y, padding)
-    assert abs(gl - ol) <= max(bound, 1e-5 * abs(ol))
+    check_loss(gl, ol, f"constant {a} {b} {padding}")
     if padding == "valid":
-        S = (2 * a * b + 1e-4) / (a * a + b * b + 1e-4)
-        assert abs((1 - gl) - S) <= max(bound, 1e-5 * abs(1 - S))
+        af, bf = float(np.float32(a)), float(np.float32(b))
+        S = (2 * af * bf + 1e-4) / (af * af + bf * bf + 1e-4)
+        assert abs(gl - (1 - S)) <= 1e-5 * abs(1 - S)
+    bar = constant_grad_bar(a, b)
     for g, og in ((g1, o1), (g2, o2)):
-        scale = float(np.abs(og).max())
         err = float(np.abs(g.astype(np.float64) - og).max())
-        assert err <= max(bound, GRAD_RTOL) * scale
+        assert err <= bar * float(np.abs(og).max()), (err, bar)
 
 
 def test_zero_against_one():
@@ -121,10 +131,58 @@ def test_zero_against_one():
     o = np.ones((1, 1, 32, 32), np.float32)
     gl, g1, g2 = gpu_run(z, o, "same")
     ol, o1, o2 = oracle.ssim_loss(z, o, "same")
-    bound = _constant_bound(0.0, 1.0)
-    assert abs(gl - ol) <= max(bound, 1e-5 * abs(ol))
+    check_loss(gl, ol, "zeros vs ones")
+    bar = constant_grad_bar(0.0, 1.0)
     for g, og in ((g1, o1), (g2, o2)):
-        assert float(np.abs(g - og).max()) <= max(bound, GRAD_RTOL) * float(np.abs(og).max())
+        assert float(np.abs(g - og).max()) <= bar * float(np.abs(og).max())
+
+
+def _flat_case(a, b, padding, what):
+    """a, b through the saved-maps pair and the one-launch step, against the
+    oracle at the contract's bars (upstream gradient 0.5)."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    ol, o1, o2 = oracle.ssim_loss(a, b, padding, dloss=0.5)
+    gl, g1, g2 = gpu_run(a, b, padding, dloss=0.5)
+    check_loss(gl, ol, f"{what} saved maps")
+    check_grad(g1, o1, f"{what} grad_img1")
+    check_grad(g2, o2, f"{what} grad_img2")
+    dev = torch.device("cuda")
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    lo, h1, h2 = S.loss_and_grad(ta, tb, padding, weight=0.5)
+    check_loss(float(lo.item()), ol, f"{what} one launch")
+    check_grad(h1.cpu().numpy(), o1, f"{what} one launch grad_img1")
+    check_grad(h2.cpu().numpy(), o2, f"{what} one launch grad_img2")
+
+
+@pytest.mark.parametrize("padding", ["valid", "same"])
+@pytest.mark.parametrize("level", FLAT_LEVELS)
+def test_flat_image_against_noisy_one(level, padding):
+    """One image flat at a level, the other a noisy copy, each way round (a
+    render flat where the reference has texture).  At 0.05 and 0.95 the
+    offset from 1/2 is inexact in fp32, and a blur of the flat image that
+    misrounded its mean would bias the covariance of every window by the same
+    amount: the loss would miss the bar by about 3e-5."""
+    for noise in (0.01, 0.001):
+        x, y = flat_pair((1, 2, 150, 190), level, noise, seed=int(level * 1000))
+        for a, b in ((x, y), (y, x)):
+            say(f"[flat] level {level:.4f} noise {noise} {padding}")
+            _flat_case(a, b, padding, f"flat {level:.4f}")
+
+
+@pytest.mark.parametrize("padding", ["valid", "same"])
+@pytest.mark.parametrize("kind,noise", [("objects", 0.01), ("objects", 0.003),
+                                        ("dark-field", 0.005), ("dark-field", 0.002)])
+def test_objects_and_dark_fields(kind, noise, padding):
+    """Flat rectangles on a black background, and dark low-contrast fields,
+    with the noise on the second image -- and swapped."""
+    for seed in range(2):
+        x, y = make_pair((1, 3, 150, 190), kind, noise, seed=400 + seed)
+        for a, b in ((x, y), (y, x)):
+            say(f"[flat] {kind} noise {noise} {padding} seed {seed}")
+            _flat_case(a, b, padding, kind)
 
 
 def test_nullable_gradients_and_dloss_scaling():
