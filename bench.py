@@ -65,6 +65,10 @@ def parse():
                     help="after the timed steps, also time the kernels of the other designs "
                          "(reported under 'designs'; on by default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other configurations (1080p-same, 4k-batch8) a default "
+                         "1080p-valid run also times (profile passes skip them, so that every "
+                         "dispatch of a kernel in the run has the workload's size)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with a cache flush before each (0 = skip)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
@@ -72,6 +76,13 @@ def parse():
                          "(an idle GPU needs some milliseconds of load to reach its clock)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (counter calibration)")
+    ap.add_argument("--profile", metavar="OUTDIR", default=None,
+                    help="run the rocprofv3 passes for --workload / --dtype (kernel trace, "
+                         "FETCH_SIZE, WRITE_SIZE, three SQ/GRBM counter groups), each a child "
+                         "process under its own time limit, writing under OUTDIR, then "
+                         "summarize them into profiles/")
+    ap.add_argument("--summarize", metavar="OUTDIR", default=None,
+                    help="only summarize the rocprofv3 CSVs a --profile run left under OUTDIR")
     return ap.parse_args()
 
 
@@ -171,6 +182,24 @@ def cpu_model():
     return None
 
 
+def host_threads():
+    """(cores this process may run on, threads the oracle uses, OMP_NUM_THREADS
+    or None): every core of the affinity mask, unless OMP_NUM_THREADS sets a
+    smaller share of the host (a GPU machine gives each GPU a share of its
+    cores)."""
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    try:
+        omp = int(omp) if omp else None
+    except ValueError:
+        omp = None
+    threads = max(1, min(ncores, omp) if omp else ncores)
+    return ncores, threads, omp
+
+
 def cpu_baseline(x, y, padding, pixels_per_image_batch, dloss):
     """The fp64 oracle, as it stands, on the host cores: whole forward +
     gradient of the same workload, repeated until about 10 s have passed
@@ -178,11 +207,7 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch, dloss):
     the baseline record and the oracle's last (loss, grad_x, grad_y)."""
     import oracle
 
-    try:
-        ncores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncores = os.cpu_count() or 1
-    threads = max(1, min(16, ncores))
+    ncores, threads, omp = host_threads()
     oracle.set_threads(threads)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -203,6 +228,9 @@ def cpu_baseline(x, y, padding, pixels_per_image_batch, dloss):
         "value": round(reps * pixels_per_image_batch / el / 1e6, 3),
         "unit": "Mpix/s",
         "cores": threads,
+        "affinity_cores": ncores,
+        "host_cpus": os.cpu_count(),
+        "omp_num_threads": omp,
         "kind": "oracle",
         "sample": f"{reps} x whole forward+gradient of the benchmark batch "
                   f"({x.shape}, {padding}) in {el:.1f} s",
@@ -350,6 +378,410 @@ def bench_volume(args, w, x, y):
     print(json.dumps(out), flush=True)
 
 
+def events_ms(fn, reps, warm=3):
+    """Average milliseconds per call of fn over reps calls back to back,
+    between two HIP events on torch's current stream (the stream the library
+    launches on)."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def roofline_fracs(shape, padding, kernel, ms, eb=4):
+    """The kernel's algorithmic fp32 rate and HBM rate per launch of ms
+    milliseconds, as fractions of the published peaks."""
+    tf = algorithmic_flops(shape, padding)[kernel] / (ms * 1e-3) / 1e12
+    gbs = algorithmic_bytes(shape, padding, eb)[kernel] / (ms * 1e-3) / 1e9
+    return {"alu": {"achieved": round(tf, 2), "unit": "TFLOP/s",
+                    "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4)},
+            "hbm": {"achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def one_launch_record(t1, t2, padding, ws, reps):
+    """The one-launch step (ssim_loss_and_grad, both gradients) on resident
+    images: per-launch time from HIP events, Mpix/s and both roofline
+    fractions."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    N, C, H, W = t1.shape
+    loss = torch.empty((), dtype=torch.float32, device=t1.device)
+    dl = torch.tensor(0.8, dtype=torch.float32, device=t1.device)
+    g1, g2 = torch.empty_like(t1), torch.empty_like(t2)
+    f = lambda: S.ssim_loss_and_grad(t1, t2, padding, dl, loss, ws, g1, g2)
+    settle(f, 200.0)
+    ms = events_ms(f, reps)
+    rec = {"shape": [N, C, H, W], "padding": padding, "launches": reps,
+           "ms_per_launch": round(ms, 5), "mpix_per_s": round(N * H * W / (ms * 1e-3) / 1e6, 1)}
+    rec.update(roofline_fracs((N, C, H, W), padding, "ssim_loss_and_grad", ms))
+    return rec
+
+
+def autograd_record(t1, t2, padding, reps):
+    """ssim_loss(img1, img2).backward() with both images requiring
+    gradients, timed three ways: the step as the GPU queue sees it (HIP
+    events around reps steps), the host's time to issue a step (autograd
+    engine and binding; no synchronisation inside the loop) and the GPU time
+    of the step's launches alone, back to back without autograd."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    a1 = t1.detach().clone().requires_grad_(True)
+    a2 = t2.detach().clone().requires_grad_(True)
+    early = 4 * t1.nbytes <= S.EARLY_GRADIENT_BYTES
+
+    def step():
+        a1.grad = None
+        a2.grad = None
+        S.ssim_loss(a1, a2, padding).backward()
+
+    settle(step, 200.0)
+    step_ms = events_ms(step, reps)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    host_ms = (time.perf_counter() - h0) * 1e3 / reps
+    torch.cuda.synchronize()
+    dev = t1.device
+    ws = S.workspace_for(dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dl = torch.ones((), dtype=torch.float32, device=dev)
+    if early:
+        gbuf = torch.empty((2,) + tuple(t1.shape), dtype=torch.float32, device=dev)
+
+        def kernels():
+            S.ssim_loss_and_grad(t1, t2, padding, dl, loss, ws, gbuf[0], gbuf[1])
+            S.ssim_grad_scale(dl, gbuf, gbuf)
+
+        launches = "ssim_loss_and_grad (upstream gradient 1) + one ssim_grad_scale over both"
+    else:
+        g1, g2 = torch.empty_like(t1), torch.empty_like(t2)
+
+        def kernels():
+            S.ssim_forward(t1, t2, padding, loss, None, ws)
+            S.ssim_backward_recompute(dl, t1, t2, padding, g1, g2)
+
+        launches = "ssim_forward (inference) + ssim_backward_recompute"
+    gpu_ms = events_ms(kernels, reps)
+    N, C, H, W = t1.shape
+    return {"ms_per_step": round(step_ms, 5), "mpix_per_s": round(N * H * W / (step_ms * 1e-3) / 1e6, 1),
+            "host_ms_per_step": round(host_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5),
+            "gradients": "both", "launches": launches, "steps": reps}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 passes and their summaries (profiles/)
+
+# The library's kernels by entry point: (kernel-name prefix without the image
+# type, entry point).  Stream and unaligned variants count for their entry.
+KERNEL_ENTRY = [
+    ("ssim_loss_grad_ref", "ssim_loss_and_grad_ref"),
+    ("ssim_loss_grad", "ssim_loss_and_grad"),
+    ("ssim_bwd_recompute", "ssim_backward_recompute"),
+    ("ssim_bwd", "ssim_backward"),
+    ("ssim_fwd_train", "ssim_forward"),
+    ("ssim_fwd_infer", "ssim_forward(inference)"),
+    ("ssim_ref_stats", "ssim_reference_stats"),
+    ("ssim3d_fwd_train", "ssim3d_forward"),
+    ("ssim3d_fwd_infer", "ssim3d_forward(inference)"),
+    ("ssim3d_bwd", "ssim3d_backward"),
+    ("ssim_grad_scale", "ssim_grad_scale"),
+]
+SQ_GROUPS = {
+    "sq_a": "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_FMA_F32 SQ_INSTS_LDS SQ_INSTS_SALU "
+            "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU",
+    "sq_b": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+            "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS",
+    "sq_c": "GRBM_GUI_ACTIVE GRBM_COUNT SQ_INSTS_VALU SQ_WAVES",
+}
+
+
+def kernel_entry(name):
+    """The entry point a kernel name belongs to, or None (other kernels)."""
+    m = re.search(r"(ssim(?:3d)?_\w*?kernel)", name)
+    if not m:
+        return None
+    base = m.group(1)
+    for prefix, entry in KERNEL_ENTRY:
+        if base.startswith(prefix):
+            rest = base[len(prefix):]
+            # the next prefix down is a longer name (ssim_bwd vs ssim_bwd_recompute)
+            if prefix == "ssim_bwd" and rest.startswith("_recompute"):
+                continue
+            if prefix == "ssim_loss_grad" and rest.startswith("_ref"):
+                continue
+            return entry
+    return None
+
+
+def profile_passes(workload, dtype, outdir):
+    """The rocprofv3 command lines of a profile of one workload (each run from
+    the repository root): the kernel trace of the whole bench (every design's
+    kernels) and one counter pass per group, on a short run with a 512 MiB
+    calibration copy."""
+    bench = ["python3", "bench.py", "--workload", workload, "--dtype", dtype, "--no-cpu",
+             "--no-workloads", "--cold-steps", "0"]
+    short = bench + ["--steps", "20", "--warmup", "3", "--settle-ms", "50"]
+    passes = {"trace": (300, ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv",
+                              "-d", f"{outdir}/trace", "-o", "run", "--"]
+                        + bench + ["--steps", "300", "--warmup", "10"])}
+    pmc = {"fetch": "FETCH_SIZE", "write": "WRITE_SIZE", **SQ_GROUPS}
+    for key, counters in pmc.items():
+        passes[key] = (120, ["rocprofv3", "--pmc", *counters.split(), "--output-format", "csv",
+                             "-d", f"{outdir}/{key}", "-o", "p", "--"]
+                       + short + ["--copy-calib", "512"])
+    return passes
+
+
+def run_profile(workload, dtype, outdir):
+    """Every pass of profile_passes, in order, each a child process under its
+    own kill-on-expiry time limit; stops at the first pass that fails.  The
+    bench line each pass prints goes to <outdir>/<pass>.log."""
+    import subprocess
+
+    os.makedirs(outdir, exist_ok=True)
+    for key, (limit, cmd) in profile_passes(workload, dtype, outdir).items():
+        print(f"[profile] {workload} {dtype} pass {key}: {' '.join(cmd)}", flush=True)
+        with open(os.path.join(outdir, f"{key}.log"), "w") as log:
+            rc = subprocess.run(["timeout", "-s", "KILL", str(limit), *cmd], cwd=ROOT, stdout=log,
+                                stderr=subprocess.STDOUT).returncode
+        # (rocprofv3 itself may end with a segmentation fault after the program's
+        # results are whole; the summary checks for them)
+        print(f"[profile] pass {key} exit {rc}", flush=True)
+        if rc not in (0, 139, -11):
+            return rc
+    return 0
+
+
+def _csv_rows(outdir, key, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for path in sorted(glob.glob(os.path.join(outdir, key, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _bench_line(outdir, key):
+    path = os.path.join(outdir, f"{key}.log")
+    if not os.path.exists(path):
+        return None
+    for line in reversed(open(path).read().splitlines()):
+        if line.startswith("{"):
+            try:
+                return json.loads(line)
+            except ValueError:
+                return None
+    return None
+
+
+def _counter_dispatches(outdir, key):
+    """Per kernel name: {counter: {dispatch: value}}, from one --pmc pass."""
+    acc = {}
+    for r in _csv_rows(outdir, key, "counter_collection.csv"):
+        name = r.get("Kernel_Name", "")
+        cnt = r.get("Counter_Name", "")
+        try:
+            val = float(r.get("Counter_Value", "nan"))
+        except ValueError:
+            continue
+        disp = r.get("Dispatch_Id", "")
+        acc.setdefault(name, {}).setdefault(cnt, {})
+        # a dispatch's value may come in several rows (per XCD or SE): sum them
+        acc[name][cnt][disp] = acc[name][cnt].get(disp, 0.0) + val
+    return acc
+
+
+def _counter_means(outdir, key):
+    """Per kernel name: {counter: mean per dispatch}, from one --pmc pass."""
+    return {n: {c: sum(d.values()) / len(d) for c, d in cs.items()}
+            for n, cs in _counter_dispatches(outdir, key).items()}
+
+
+def _per_entry(means):
+    """Counter means by entry point (the dispatch-weighted mean over its
+    kernel variants present in the run; one variant runs per workload)."""
+    out = {}
+    for name, cs in means.items():
+        e = kernel_entry(name)
+        if e is not None:
+            out.setdefault(e, cs)
+    return out
+
+
+def summarize_profile(workload, dtype, outdir, profiles_dir=PROFILES):
+    """Writes profiles/ssim_kernels_<tag>_kernel_trace.md, hbm_traffic_<tag>.json
+    and sq_counters_<tag>.json (+ .md) from a --profile run's CSVs, tag =
+    workload, with -<dtype> for half types.  FETCH_SIZE and WRITE_SIZE are
+    scaled by what they read for the 512 MiB calibration copy."""
+    tag = workload if dtype == "float32" else f"{workload}-{dtype}"
+    sha = source_hash()
+    passes = profile_passes(workload, dtype, "OUT")
+    cmd = lambda key: " ".join(passes[key][1]).replace("OUT", os.path.relpath(outdir, ROOT))
+    os.makedirs(profiles_dir, exist_ok=True)
+
+    # kernel trace
+    stats = _csv_rows(outdir, "trace", "kernel_stats.csv")
+    trace = _csv_rows(outdir, "trace", "kernel_trace.csv")
+    lines = [f"# rocprofv3 kernel trace: {workload} ({dtype} images)", "",
+             "Command (from the repository root, on the MI355X):", "", "```", cmd("trace"), "```",
+             "", f"Library code sha256[:16] (ssim_loss_amd/csrc and include, comments dropped): "
+             f"`{sha}`", "", "| kernel | entry point | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r.get("Name", r.get("Kernel_Name", ""))
+        try:
+            calls = int(r["Calls"])
+            avg, mn, mx = (float(r[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs"))
+            share = float(r.get("Percentage", "nan"))
+        except (KeyError, ValueError):
+            continue
+        lines.append(f"| {name[:60]} | {kernel_entry(name) or '-'} | {calls} | {avg:.2f} | "
+                     f"{mn:.2f} | {mx:.2f} | {share:.1f}% |")
+    # runs of one kernel launched back to back (bench times each entry point's
+    # launches between HIP events after the timed steps)
+    runs = []
+    for r in sorted(trace, key=lambda r: int(r.get("Start_Timestamp", 0))):
+        name = r.get("Kernel_Name", "")
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == name:
+            runs[-1][1].append(dur)
+        else:
+            runs.append([name, [dur]])
+    lines += ["", "The same dispatches as runs of one kernel launched back to back, in launch order "
+              "(runs of fewer than 6 left out):", "", "| order | kernel | launches | average (us) | "
+              "median (us) |", "|---|---|---|---|---|"]
+    k = 0
+    for name, durs in runs:
+        if len(durs) < 6:
+            continue
+        k += 1
+        durs = sorted(durs)
+        lines.append(f"| {k} | {kernel_entry(name) or name[:40]} | {len(durs)} | "
+                     f"{sum(durs) / len(durs):.2f} | {durs[len(durs) // 2]:.2f} |")
+    line = _bench_line(outdir, "trace")
+    if line:
+        lines += ["", "The bench line printed by the profiled run: "
+                  f"{line.get('value')} {line.get('unit')}, {line.get('ms_per_step', 0) * 1e3:.2f} us "
+                  f"per step; kernels_ms " + ", ".join(f"{k} {v * 1e3:.2f} us" for k, v in
+                                                       line.get("kernels_ms", {}).items()) + "."]
+    with open(os.path.join(profiles_dir, f"ssim_kernels_{tag}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic
+    fetch = _counter_means(outdir, "fetch")
+    write = _counter_means(outdir, "write")
+
+    # the calibration copy: the largest single dispatch of a copy kernel (the
+    # run's other copies are small staging copies)
+    def calib(key, cnt):
+        vals = [v for n, cs in _counter_dispatches(outdir, key).items() if "copy" in n.lower()
+                for v in cs.get(cnt, {}).values()]
+        return max(vals) if vals else None
+
+    f_cal, w_cal = calib("fetch", "FETCH_SIZE"), calib("write", "WRITE_SIZE")
+    traffic = None
+    if f_cal and w_cal:
+        fs, wsc = 524288.0 / f_cal, 524288.0 / w_cal
+        fe, we = _per_entry(fetch), _per_entry(write)
+        detail = {e: {"read_bytes": int(fe[e]["FETCH_SIZE"] * 1024 * fs),
+                      "write_bytes": int(we[e]["WRITE_SIZE"] * 1024 * wsc)}
+                  for e in fe if e in we and "FETCH_SIZE" in fe[e] and "WRITE_SIZE" in we[e]}
+        traffic = {"workload": workload, "dtype": dtype, "source_sha256_16": sha,
+                   "fetch_scale": round(fs, 4), "write_scale": round(wsc, 4),
+                   "calibration": f"torch copy of 512 MiB: FETCH_SIZE {f_cal:.0f} KiB, WRITE_SIZE "
+                                  f"{w_cal:.0f} KiB per dispatch",
+                   "commands": [cmd("fetch"), cmd("write")],
+                   "bytes_per_launch": {e: d["read_bytes"] + d["write_bytes"] for e, d in detail.items()},
+                   "detail": detail}
+        with open(os.path.join(profiles_dir, f"hbm_traffic_{tag}.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+
+    # SQ / GRBM counters
+    sq = {}
+    for key in SQ_GROUPS:
+        for e, cs in _per_entry(_counter_means(outdir, key)).items():
+            sq.setdefault(e, {}).update(cs)
+    kernel_us = {}
+    for r in stats:
+        e = kernel_entry(r.get("Name", ""))
+        if e is not None:
+            kernel_us.setdefault(e, float(r["AverageNs"]) / 1e3)
+    derived = {}
+    for e, c in sq.items():
+        d = {}
+        g = lambda k: c.get(k)
+        if g("SQ_INSTS_VALU") and g("SQ_WAVES"):
+            d["valu_insts_per_wave"] = round(g("SQ_INSTS_VALU") / g("SQ_WAVES"), 1)
+        if g("SQ_ACTIVE_INST_VALU") and g("SQ_WAVE_CYCLES"):
+            d["valu_active_share_of_wave_cycles"] = round(g("SQ_ACTIVE_INST_VALU") / g("SQ_WAVE_CYCLES"), 4)
+        if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE"):
+            d["lds_bank_conflict_share_of_lds_active"] = round(g("SQ_LDS_BANK_CONFLICT") / g("SQ_LDS_IDX_ACTIVE"), 4)
+        if g("SQ_WAIT_INST_ANY") and g("SQ_WAVE_CYCLES"):
+            d["wait_share_of_wave_cycles"] = round(g("SQ_WAIT_INST_ANY") / g("SQ_WAVE_CYCLES"), 4)
+        if g("SQ_WAIT_INST_LDS") and g("SQ_WAVE_CYCLES"):
+            d["lds_wait_share_of_wave_cycles"] = round(g("SQ_WAIT_INST_LDS") / g("SQ_WAVE_CYCLES"), 4)
+        if g("SQ_INSTS_VALU_FMA_F32") and g("SQ_INSTS_VALU"):
+            d["fma_f32_share_of_valu"] = round(g("SQ_INSTS_VALU_FMA_F32") / g("SQ_INSTS_VALU"), 4)
+        us = kernel_us.get(e)
+        if us and g("GRBM_GUI_ACTIVE"):
+            ghz = g("GRBM_GUI_ACTIVE") / 8 / (us * 1e3)
+            d["clock_ghz"] = round(ghz, 3)
+            if g("SQ_INSTS_VALU"):
+                d["valu_insts_per_cu_per_cycle"] = round(g("SQ_INSTS_VALU") / 256 / (us * 1e3 * ghz), 3)
+        if us and g("SQ_INSTS_VALU"):
+            d["valu_insts_per_cu_per_ns"] = round(g("SQ_INSTS_VALU") / 256 / (us * 1e3), 3)
+        if us and traffic and e in traffic["bytes_per_launch"]:
+            d["counter_gbs"] = round(traffic["bytes_per_launch"][e] / (us * 1e-6) / 1e9, 1)
+        if us:
+            d["trace_avg_us"] = round(us, 2)
+        derived[e] = d
+    sqrec = {"workload": workload, "dtype": dtype, "source_sha256_16": sha,
+             "commands": [cmd(k) for k in SQ_GROUPS], "counters": sq, "derived": derived}
+    with open(os.path.join(profiles_dir, f"sq_counters_{tag}.json"), "w") as f:
+        json.dump(sqrec, f, indent=1)
+    md = [f"# SQ and GRBM counters per launch (rocprofv3 --pmc): {workload}, {dtype} images", "",
+          "Commands (each pass in a run of its own, under `timeout -s KILL 120`):", "", "```",
+          *[cmd(k) for k in SQ_GROUPS], "```", "",
+          f"Library code sha256[:16]: `{sha}`. Each counter is the per-dispatch value summed over "
+          "the chip, averaged over the dispatches of the run; SQ_WAVE_CYCLES, SQ_ACTIVE_INST_* and "
+          "SQ_WAIT_INST_* count in one unit, so only their ratios are used; GRBM_GUI_ACTIVE / 8 / "
+          "(the kernel's trace average) gives the clock the launch ran at.", ""]
+    for e, d in derived.items():
+        md.append(f"- **{e}**: " + ", ".join(f"{k} {v}" for k, v in d.items()))
+    with open(os.path.join(profiles_dir, f"ssim_kernels_{tag}_sq_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(f"[summarize] wrote profiles for {tag} (source {sha})", flush=True)
+
+
+def committed_counters(args, kernel):
+    """The dominant kernel's derived counter figures from the committed
+    profiles/sq_counters_<tag>.json, or None when there is none for this
+    workload and dtype or it belongs to other kernel sources."""
+    tag = args.workload if args.dtype == "float32" else f"{args.workload}-{args.dtype}"
+    path = os.path.join(PROFILES, f"sq_counters_{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("derived", {}).get(kernel)
+
+
 DESIGNS = {
     # design: the launches of one step
     "saved": ("ssim_forward", "ssim_backward"),
@@ -363,6 +795,14 @@ DESIGNS = {
 
 def main():
     args = parse()
+    if args.summarize or args.profile:
+        outdir = os.path.abspath(args.summarize or args.profile)
+        if args.profile:
+            rc = run_profile(args.workload, args.dtype, outdir)
+            if rc != 0:
+                sys.exit(rc)
+        summarize_profile(args.workload, args.dtype, outdir)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by image planes with one scalar all-reduce, which is not built",
@@ -448,24 +888,11 @@ def main():
              and (args.all_kernels or k in DESIGNS[args.design])]
     kern = {k: per_launch_ms(launches[k]) for k in timed}
 
-    # the autograd path (ssim_loss(...).backward() on fp32 images: the
-    # one-launch kernel with an upstream gradient of 1 in the forward, the
-    # gradient scaled in the backward, with torch's autograd bookkeeping),
-    # timed with events around K whole steps
+    # the autograd path (ssim_loss(...).backward(), both gradients) at this
+    # size; the default run adds the 4K batch below
     autograd = None
     if args.all_kernels and args.dtype == "float32":
-        a1 = t1.detach().clone().requires_grad_(True)
-
-        def ag_step():
-            a1.grad = None
-            S.ssim_loss(a1, t2, w.padding).backward()
-
-        for _ in range(5):
-            ag_step()
-        torch.cuda.synchronize()
-        ag_ms = per_launch_ms(ag_step)
-        autograd = {"ms_per_step": round(ag_ms, 5), "mpix_per_s": round(mpix / (ag_ms * 1e-3), 1),
-                    "launches": "ssim_loss_and_grad (upstream gradient 1) + ssim_grad_scale"}
+        autograd = {args.workload: autograd_record(t1, t2, w.padding, min(K, 500))}
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
@@ -577,6 +1004,7 @@ def main():
                     "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                     "algorithmic_flops": flops[dom]},
         }),
+        "counters": committed_counters(args, dom),
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "designs": designs,
         "autograd": autograd,
@@ -589,6 +1017,25 @@ def main():
         },
         "loss": float(loss.item()),
     }
+    # the other configurations the target names, timed in this run: the
+    # one-launch step on 1080p with same padding and on the 8 x 4K batch (and
+    # the autograd step on the batch)
+    if (args.all_kernels and args.dtype == "float32" and args.workload == "1080p-valid"
+            and not args.no_workloads):
+        out["workloads"] = {}
+        for name in ("1080p-same", "4k-batch8"):
+            wl = WORKLOADS[name]
+            xo, yo = make_workload(name)
+            u1 = torch.from_numpy(xo).to(dev)
+            u2 = torch.from_numpy(yo).to(dev)
+            del xo, yo
+            reps = 1000 if u1.numel() < 1e7 else 40
+            out["workloads"][name] = one_launch_record(u1, u2, wl.padding, ws, reps)
+            if name == "4k-batch8":
+                out["autograd"][name] = autograd_record(u1, u2, wl.padding, 20)
+            del u1, u2
+            torch.cuda.empty_cache()
+
     if not args.no_cpu:
         # the oracle gets the values the GPU read (half-precision inputs rounded)
         xo = t1.float().cpu().numpy()

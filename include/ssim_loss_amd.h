@@ -251,12 +251,14 @@ size_t ssim_noalloc_scratch_bytes(void);
  *   dloss  : device fp32 scalar, the upstream gradient
  *   grad   : device fp32 array of n elements (input), 4-byte aligned
  *   out    : device fp32 array of n elements (output, overwritten); may be
- *            grad itself (in place), must not otherwise overlap it
+ *            grad itself (in place), must not otherwise overlap it, and must
+ *            not contain dloss
  *   n      : element count; 0 launches nothing
  *   stream : hipStream_t (NULL = default stream)
  * Returns SSIM_ERR_SHAPE for n < 0 or a pointer not 4-byte aligned,
  * SSIM_ERR_NULL for a NULL pointer with n > 0, SSIM_ERR_OVERFLOW when 4 n
- * bytes overflow and SSIM_ERR_ALIAS for a partial overlap, all before any
+ * bytes overflow and SSIM_ERR_ALIAS for a partial overlap of out and grad or
+ * for dloss inside out, all before any
  * HIP call; SSIM_ERR_DEVICE on a device that is not gfx950; SSIM_ERR_HIP if
  * the launch fails. */
 int ssim_grad_scale(const float* dloss, const float* grad, float* out, int64_t n, void* stream);

@@ -445,14 +445,19 @@ def _make_function():
             ctx.train = train
             ctx.recompute = recompute
             ctx.dev = dev
-            # fp32 images whose gradient is wanted: the gradients with an
-            # upstream gradient of 1, in the launch that forms the loss; the
-            # backward only scales them (bit for bit the one-launch result)
-            ctx.early = bool(train and recompute and grads and img1.dtype == torch.float32)
+            # fp32 images whose gradient is wanted, while the step stays in the
+            # last-level cache: the gradients with an upstream gradient of 1,
+            # in the launch that forms the loss; the backward scales them in
+            # place (bit for bit the one-launch result).  Both gradients share
+            # one buffer, so one scale launch serves both.
+            ctx.early = bool(train and recompute and grads and img1.dtype == torch.float32
+                             and 4 * img1.nbytes <= EARLY_GRADIENT_BYTES)
             if ctx.early:
                 want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
-                g1 = torch.empty_like(img1) if want1 else None
-                g2 = torch.empty_like(img2) if want2 else None
+                gbuf = torch.empty((int(want1) + int(want2),) + tuple(img1.shape),
+                                   dtype=torch.float32, device=dev)
+                g1 = gbuf[0] if want1 else None
+                g2 = gbuf[-1] if want2 else None
                 # ssim_loss checked the images; the other buffers are made here
                 N, C, H, W = img1.shape
                 rc = lib().ssim_loss_and_grad(
@@ -461,7 +466,10 @@ def _make_function():
                     workspace_for(dev).data_ptr(), _dptr(g1), _dptr(g2), _current_stream(dev.index))
                 if rc != SSIM_OK:
                     raise SsimError(rc, "ssim_loss_and_grad")
-                ctx.save_for_backward(g1, g2)
+                # (an intermediate, kept on ctx: the backward scales it in place)
+                ctx.gbuf = gbuf
+                ctx.scaled = False
+                ctx.save_for_backward(img1, img2)
                 return loss
             maps = alloc_saved_maps(img1, padding) if train and not recompute else None
             N, C, H, W = img1.shape
@@ -484,19 +492,21 @@ def _make_function():
                 raise RuntimeError("ssim_loss was called with train=False; no gradient saved")
             want1, want2 = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
             dl = dloss.detach().to(device=ctx.dev, dtype=torch.float32).reshape(()).contiguous()
-            if ctx.early:
-                e1, e2 = ctx.saved_tensors
-                outs = []
-                for want, e in ((want1, e1), (want2, e2)):
-                    g = None
-                    if want and e is not None:
-                        g = torch.empty_like(e)
-                        rc = lib().ssim_grad_scale(dl.data_ptr(), e.data_ptr(), g.data_ptr(),
-                                                   e.numel(), _current_stream(e.device.index))
-                        if rc != SSIM_OK:
-                            raise SsimError(rc, "ssim_grad_scale")
-                    outs.append(g)
-                return outs[0], outs[1], None, None, None, None
+            if ctx.early and not ctx.scaled:
+                # the first backward scales the gradients in place, in one
+                # launch over both
+                gbuf = ctx.gbuf
+                ctx.gbuf = None
+                ctx.scaled = True
+                rc = lib().ssim_grad_scale(dl.data_ptr(), gbuf.data_ptr(), gbuf.data_ptr(),
+                                           gbuf.numel(), _current_stream(gbuf.device.index))
+                if rc != SSIM_OK:
+                    raise SsimError(rc, "ssim_grad_scale")
+                g1 = gbuf[0] if want1 else None
+                g2 = gbuf[-1] if want2 else None
+                return g1, g2, None, None, None, None
+            # (a second backward through an early step, retain_graph=True, forms
+            # the gradients again from the images)
             if ctx.recompute:
                 img1, img2 = ctx.saved_tensors
             else:
@@ -524,15 +534,24 @@ def _make_function():
 
 _fn = None
 
+# Above this many bytes of images and gradients (4 image-size buffers) a step
+# cannot stay in the 256 MB last-level cache between its forward and backward:
+# there the inference forward and the recomputing backward cost less GPU time
+# than the one-launch forward plus the scale pass, and hold no gradient
+# buffers between the two.
+EARLY_GRADIENT_BYTES = 256 << 20
+
 
 def ssim_loss(img1, img2, padding: str = "valid", train: bool = True, recompute: bool = True):
     """loss = 1 - mean SSIM (a 0-d fp32 tensor on the images' device), with
     gradients for whichever of img1 / img2 requires them.  With recompute
     (the default) no blurred statistics are kept between forward and
-    backward.  For fp32 images whose gradient is wanted, the forward forms
-    the loss and the gradients (for an upstream gradient of 1) in one launch
-    and the backward multiplies them by the upstream gradient, giving
-    ssim_loss_and_grad's result bit for bit; otherwise the forward forms the
+    backward.  For fp32 images whose gradient is wanted, up to
+    EARLY_GRADIENT_BYTES of images and gradients, the forward forms the loss
+    and the gradients (for an upstream gradient of 1) in one launch and the
+    backward multiplies them by the upstream gradient in place, giving
+    ssim_loss_and_grad's result bit for bit (the gradients are formed under
+    grad mode even if no backward follows); otherwise the forward forms the
     loss alone and the backward forms the statistics again from the images.
     recompute=False saves the four blurred statistics (16 bytes per map
     entry) for the backward to read, as the pages' training mode does.  All

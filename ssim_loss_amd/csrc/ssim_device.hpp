@@ -263,6 +263,9 @@ struct Params {
   int map_h, map_w;
   int vpitch;
   int64_t planes;
+  // share of a workgroup dispatched first onto its CU, against one dispatched
+  // second, in hundredths (100: equal shares); see fused_share
+  int first_w;
 };
 
 // ---------------------------------------------------------------------------

@@ -382,11 +382,21 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
   __syncthreads();
 }
 
-// This workgroup's share: an equal contiguous run of a sequence in which
-// each strip-column counts as its kWarm warm-up rows followed by its
-// gradient rows, so a share that starts a strip-column is charged for the
-// warm-up it pays; a share that starts inside one pays at most kWarm more.
-// The share is taken as one segment per strip-column it touches.
+// This workgroup's share: a contiguous run of a sequence in which each
+// strip-column counts as its kWarm warm-up rows followed by its gradient
+// rows, so a share that starts a strip-column is charged for the warm-up it
+// pays; a share that starts inside one pays at most kWarm more.  The share is
+// taken as one segment per strip-column it touches.
+//
+// With two workgroups per CU (a grid of 2 x CUs, every workgroup resident at
+// once), the one dispatched first onto a CU issues ahead of the other, which
+// takes the issue slots left over, so the pair would finish far apart and the
+// second would run its last part alone (per tick, a lone workgroup gets 0.62
+// of what the pair does together).  The first therefore takes first_w / 100
+// times the second's share.  Dispatch hands consecutive workgroup ids to the
+// 8 XCDs in turn and, within an XCD, to its CUs in turn: ids below G / 2 are
+// the first on their CU, which logical_block makes the first half of each
+// XCD's run.  first_w == 100 gives equal shares.
 struct FShare {
   int64_t v, v_end, vlen;
 };
@@ -397,8 +407,20 @@ __device__ __forceinline__ FShare fused_share(const Params& p) {
   w.vlen = (int64_t)p.out_h + kWarm;
   const int64_t total = p.cols * w.vlen;
   const int64_t lb = logical_block();
-  w.v = lb * total / gridDim.x;
-  w.v_end = (lb + 1) * total / gridDim.x;
+  const int64_t G = gridDim.x;
+  if (p.first_w == 100 || G % 8 != 0) {
+    w.v = lb * total / G;
+    w.v_end = (lb + 1) * total / G;
+    return w;
+  }
+  const int64_t m = G / 8, h = m / 2;  // workgroups per XCD, of which first on a CU
+  const int64_t x = lb / m, k = lb - x * m;
+  const int64_t fw = p.first_w;
+  // weight of the first kk workgroups of an XCD's run
+  const auto cum = [&](int64_t kk) { return fw * (kk < h ? kk : h) + 100 * (kk > h ? kk - h : 0); };
+  const int64_t per = cum(m);
+  w.v = (x * per + cum(k)) * total / (8 * per);
+  w.v_end = (x * per + cum(k + 1)) * total / (8 * per);
   return w;
 }
 

@@ -212,6 +212,9 @@ def test_grad_scale_argument_errors_return_before_any_hip_call():
     assert f(0x1000, 0x10000, 0x10000 + 16, 8) == -5     # partial overlap
     assert f(0x1000, 0x10000, 0x10000 - 16, 8) == -5
     assert f(0x1000, 0x10000, 0x20000, 1 << 62) == -4
+    assert f(0x20000 + 16, 0x10000, 0x20000, 8) == -5     # dloss inside out
+    assert f(0x20000 + 28, 0x10000, 0x20000, 8) == -5     # its last element
+    assert f(0x10000 + 8, 0x10000, 0x10000, 8) == -5     # in place, dloss inside
 
 
 def test_reference_argument_errors_return_before_any_hip_call():

@@ -202,3 +202,71 @@ def test_workload_table_matches_the_benchmark_configurations():
     assert shapes["4k-batch8"] == ((8, 3, 2160, 3840), "valid")
     assert WORKLOADS["4k-batch8"].per_image_seed
     assert WORKLOADS["1080p-valid"].kind == "field" and WORKLOADS["4k-batch8"].kind == "uniform"
+
+
+def test_profile_summaries_from_rocprof_csvs(tmp_path):
+    """bench.py --summarize: the kernel-trace table, the HBM traffic scaled by
+    the 512 MiB calibration copy, and the derived SQ figures, from CSVs laid
+    out as a --profile run leaves them (synthetic values)."""
+    import csv
+    import json
+
+    import bench
+
+    out = tmp_path / "prof"
+
+    def write(key, fname, rows):
+        d = out / key / "host" / "123"
+        d.mkdir(parents=True, exist_ok=True)
+        with open(d / fname, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=list(rows[0]))
+            w.writeheader()
+            w.writerows(rows)
+
+    k = "(anonymous namespace)::ssim_loss_grad_kernel(ssim_dev::Params)"
+    cp = "void at::native::vectorized_elementwise_kernel<4, copy_kernel...>"
+    write("trace", "run_kernel_stats.csv",
+          [{"Name": k, "Calls": "10", "TotalDurationNs": "500000", "AverageNs": "50000",
+            "Percentage": "90.0", "MinNs": "49000", "MaxNs": "51000"}])
+    write("trace", "run_kernel_trace.csv",
+          [{"Kernel_Name": k, "Start_Timestamp": str(100 * i), "End_Timestamp": str(100 * i + 50)}
+           for i in range(8)])
+
+    def pmc(key, counter, kval, cval):
+        rows = [{"Dispatch_Id": str(i), "Kernel_Name": k, "Counter_Name": counter,
+                 "Counter_Value": str(kval)} for i in range(4)]
+        rows += [{"Dispatch_Id": str(10 + i), "Kernel_Name": cp, "Counter_Name": counter,
+                  "Counter_Value": str(cval)} for i in range(3)]
+        # small staging copies of the same kernel must not dilute the calibration
+        rows += [{"Dispatch_Id": str(20 + i), "Kernel_Name": cp, "Counter_Name": counter,
+                  "Counter_Value": "2.5"} for i in range(4)]
+        write(key, "p_counter_collection.csv", rows)
+
+    pmc("fetch", "FETCH_SIZE", 50000, 262144)   # the copy reads half: scale 2
+    pmc("write", "WRITE_SIZE", 48828.125, 524288)
+    rows = []
+    for i in range(4):
+        for c, v in (("SQ_WAVES", 4096), ("SQ_INSTS_VALU", 3.0e7), ("SQ_WAVE_CYCLES", 8.0e7),
+                     ("SQ_ACTIVE_INST_VALU", 2.4e7)):
+            rows.append({"Dispatch_Id": str(i), "Kernel_Name": k, "Counter_Name": c,
+                         "Counter_Value": str(v)})
+    write("sq_a", "p_counter_collection.csv", rows)
+    write("sq_c", "p_counter_collection.csv",
+          [{"Dispatch_Id": "0", "Kernel_Name": k, "Counter_Name": "GRBM_GUI_ACTIVE",
+            "Counter_Value": str(8 * 2.4e9 * 50e-6)}])
+
+    prof = tmp_path / "profiles"
+    bench.summarize_profile("1080p-valid", "float32", str(out), profiles_dir=str(prof))
+    tr = json.loads((prof / "hbm_traffic_1080p-valid.json").read_text())
+    assert tr["fetch_scale"] == 2.0 and tr["write_scale"] == 1.0
+    assert tr["detail"]["ssim_loss_and_grad"]["read_bytes"] == 50000 * 1024 * 2
+    assert tr["bytes_per_launch"]["ssim_loss_and_grad"] == 50000 * 2048 + 50000000
+    assert tr["source_sha256_16"] == bench.source_hash()
+    sq = json.loads((prof / "sq_counters_1080p-valid.json").read_text())
+    d = sq["derived"]["ssim_loss_and_grad"]
+    assert d["valu_insts_per_wave"] == round(3.0e7 / 4096, 1)
+    assert d["valu_active_share_of_wave_cycles"] == 0.3
+    assert abs(d["clock_ghz"] - 2.4) < 1e-3
+    assert d["trace_avg_us"] == 50.0
+    md = (prof / "ssim_kernels_1080p-valid_kernel_trace.md").read_text()
+    assert "ssim_loss_and_grad" in md and "| 10 | 50.00 |" in md
