@@ -32,9 +32,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        build()
-    lib = ctypes.CDLL(LIB_PATH)
+    path = os.environ.get("SSIM_ORACLE_LIB")  # another build, e.g. a sanitised one
+    if path is None:
+        path = LIB_PATH
+        if not os.path.exists(path):
+            build()
+    lib = ctypes.CDLL(path)
     i64, dbl, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_int
     vp = ctypes.c_void_p
     lib.oracle_taps.argtypes = [vp]

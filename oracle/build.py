@@ -13,15 +13,18 @@ SRC = os.path.join(HERE, "ssim_oracle.c")
 LIB_PATH = os.path.join(HERE, "libssim_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, SRC, "-lm"]
+def build(verbose: bool = False, cc: str = "gcc", extra: list[str] | None = None,
+          lib_path: str = LIB_PATH) -> str:
+    """Compile the oracle into lib_path.  A variant build (another compiler,
+    sanitizer flags in `extra`) names its own lib_path."""
+    tmp = lib_path + ".tmp"
+    cmd = [cc, "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           *(extra or []), "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -72,17 +72,20 @@ def lib() -> ctypes.CDLL:
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB_PATH):
+        # SSIM_LOSS_AMD_LIB names another build of the same sources (e.g. one
+        # with host-side sanitizers); there is never a fallback implementation
+        path = os.environ.get("SSIM_LOSS_AMD_LIB", LIB_PATH)
+        if not os.path.exists(path):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it first (python -m ssim_loss_amd.build "
+                f"{path} is missing: build it first (python -m ssim_loss_amd.build "
                 "or __graft_entry__.build()); there is no fallback implementation")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
         L.ssim_abi_version.restype = i32
         L.ssim_abi_version.argtypes = []
         if L.ssim_abi_version() != ABI_VERSION:
             raise ImportError(
-                f"{LIB_PATH} implements ABI version {L.ssim_abi_version()}, these bindings "
+                f"{path} implements ABI version {L.ssim_abi_version()}, these bindings "
                 f"version {ABI_VERSION}: rebuild it")
         L.ssim_strerror.restype = ctypes.c_char_p
         L.ssim_strerror.argtypes = [i32]

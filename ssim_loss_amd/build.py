@@ -43,12 +43,16 @@ def compile_flags(extra: list[str] | None = None) -> list[str]:
             *(extra or [])]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra: list[str] | None = None, build_dir: str = BUILD_DIR,
+          lib_path: str = LIB_PATH) -> str:
+    """Compile every csrc/*.hip and link lib_path.  `extra` compile flags go
+    to every translation unit (a variant build, e.g. with host-side
+    sanitizers, names its own build_dir and lib_path)."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         cmd = [cc, *compile_flags(extra), "-c", "-o", obj, src]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -57,13 +61,13 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as pool:
         objs = list(pool.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
