@@ -685,12 +685,14 @@ def summarize_profile(workload, dtype, outdir, profiles_dir=PROFILES):
     fetch = _counter_means(outdir, "fetch")
     write = _counter_means(outdir, "write")
 
-    # the calibration copy: the largest single dispatch of a copy kernel (the
-    # run's other copies are small staging copies)
+    # the calibration copies: copy_calibration's three device copies, the last
+    # three large copy dispatches of the run (earlier ones stage the inputs
+    # from the host and can be larger; the small ones move scalars)
     def calib(key, cnt):
-        vals = [v for n, cs in _counter_dispatches(outdir, key).items() if "copy" in n.lower()
-                for v in cs.get(cnt, {}).values()]
-        return max(vals) if vals else None
+        disp = sorted((int(i), v) for n, cs in _counter_dispatches(outdir, key).items()
+                      if "copy" in n.lower() for i, v in cs.get(cnt, {}).items())
+        big = [v for _, v in disp if v >= 1024.0]
+        return sorted(big[-3:])[len(big[-3:]) // 2] if len(big) >= 3 else None
 
     f_cal, w_cal = calib("fetch", "FETCH_SIZE"), calib("write", "WRITE_SIZE")
     traffic = None
@@ -709,6 +711,28 @@ def summarize_profile(workload, dtype, outdir, profiles_dir=PROFILES):
                    "detail": detail}
         with open(os.path.join(profiles_dir, f"hbm_traffic_{tag}.json"), "w") as f:
             json.dump(traffic, f, indent=1)
+        from ssim_loss_amd.inputs import WORKLOADS
+
+        w = WORKLOADS[workload]
+        eb = 4 if dtype == "float32" else 2
+        algo = (volume_algorithmic(w.shape, w.padding, eb)[0] if len(w.shape) == 5
+                else algorithmic_bytes(w.shape, w.padding, eb))
+        md = [f"# HBM traffic per launch (rocprofv3 --pmc): {workload}, {dtype} images", "",
+              "Commands:", "", "```", cmd("fetch"), cmd("write"), "```", "",
+              f"Library code sha256[:16]: `{sha}`", "",
+              f"Calibration: a torch device copy of 512 MiB in the same process reads FETCH_SIZE = "
+              f"{f_cal:.0f} KiB and WRITE_SIZE = {w_cal:.0f} KiB per dispatch, so FETCH_SIZE is "
+              f"scaled by {fs:.3f} and WRITE_SIZE by {wsc:.3f}.", "",
+              "| kernel | read MB | write MB | traffic MB | algorithmic MB | traffic / algorithmic |",
+              "|---|---|---|---|---|---|"]
+        for e, d in detail.items():
+            tot = d["read_bytes"] + d["write_bytes"]
+            a = algo.get(e)
+            md.append(f"| {e} | {d['read_bytes'] / 1e6:.1f} | {d['write_bytes'] / 1e6:.1f} | "
+                      f"{tot / 1e6:.1f} | {'-' if a is None else f'{a / 1e6:.1f}'} | "
+                      f"{'-' if not a else f'{tot / a:.3f}'} |")
+        with open(os.path.join(profiles_dir, f"ssim_kernels_{tag}_hbm_traffic.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
 
     # SQ / GRBM counters
     sq = {}
