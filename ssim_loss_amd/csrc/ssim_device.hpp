@@ -176,24 +176,31 @@ __device__ __forceinline__ float blur11_plain(const W& w) {
   return acc;
 }
 
-// Four adjacent outputs of one row from the 14 inputs v[0] .. v[13] (output
-// u reads v[u] .. v[u + 10]), by parts (kParts: the 13 differences shared
-// by the four) or plain.
-template <bool kParts>
-__device__ __forceinline__ void blur4(const float (&v)[16], float (&o)[4]) {
+// N adjacent outputs of one row from the N + 10 inputs v[0] .. v[N + 9]
+// (output u reads v[u] .. v[u + 10]), by parts (kParts: the N + 9
+// differences shared by the N outputs) or plain.
+template <bool kParts, int N, int M>
+__device__ __forceinline__ void blur_row(const float (&v)[M], float (&o)[N]) {
+  static_assert(M >= N + 10, "N outputs read N + 10 inputs");
   if constexpr (kParts) {
-    // tap by tap across the four outputs (the order blur11_by_parts takes),
-    // so that each difference is formed once and only a few are live
+    // tap by tap across the outputs (the order blur11_by_parts takes), so
+    // that each difference is formed once and only a few are live
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = v[u + 10];
+    for (int u = 0; u < N; ++u) o[u] = v[u + 10];
 #pragma unroll
     for (int j = 1; j < 11; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] = __builtin_fmaf(-head(j), v[u + j] - v[u + j - 1], o[u]);
+      for (int u = 0; u < N; ++u) o[u] = __builtin_fmaf(-head(j), v[u + j] - v[u + j - 1], o[u]);
   } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = blur11_plain([&](int a) { return v[u + a]; });
+    for (int u = 0; u < N; ++u) o[u] = blur11_plain([&](int a) { return v[u + a]; });
   }
+}
+
+// Four adjacent outputs from v[0] .. v[13] (the last two of the 16 unused).
+template <bool kParts>
+__device__ __forceinline__ void blur4(const float (&v)[16], float (&o)[4]) {
+  blur_row<kParts>(v, o);
 }
 
 // The forward's four quantities (y, x - y, (x - y)^2 and x' y') are blurred

@@ -37,17 +37,32 @@ constexpr int kVIn = kVT + 10;    // input tile columns
 constexpr int kVInY = kVTy + 10;  // input tile rows
 constexpr int kVInP = kVIn + 2;   // LDS row pitch of the input tile (16-byte rows)
 constexpr int kVByP = (kVInY + 3) / 4 * 4;  // column pitch of the X-blurred tile (16-byte columns)
+constexpr int kVAq = (kVInY * kVInP + 63) / 64 * 64;  // quantity stride of the input tile
+constexpr int kVCq = kVTy * kVT + 16;       // quantity stride of the transpose tile
 constexpr int kVThreads = kVT * kVTy;    // one output position per lane
 constexpr int kVWaves = kVThreads / kWave;
 constexpr int kVMinSlices = 16;   // shortest depth range of one workgroup
+constexpr int kXOut = 8;          // outputs of one X-pass task
+constexpr int kXGroups = kVT / kXOut;
+constexpr int kXRows = (kVInY + 15) / 16 * 16;  // X-pass rows per quantity, 16-lane aligned
+constexpr int kXTasks = kXGroups * kQ * kXRows;
+constexpr int kVHalf = 28;        // staged elements per half-wave
 static_assert(kVThreads % kWave == 0, "whole waves");
-static_assert(kVInP % 4 == 0 && kVT % 4 == 0 && 4 * (kVT / 4 - 1) + 16 <= kVInP,
+static_assert(kXTasks <= kVThreads && (kQ * kXRows) % kWave == 0,
+              "one X-pass task per lane at most; each column group starts a wave");
+static_assert(kVAq % 64 == 0 && (kXRows * kVInP) % 64 == 0,
+              "X-pass lanes 16 apart read the same bank groups, across quantities too");
+static_assert(kVHalf + 4 <= 32 && 2 * kVIn >= kVHalf && kVInP == kVIn + 2,
+              "28 consecutive staged elements span at most 32 words of the tile");
+static_assert(kVInP % 4 == 0 && kXOut % 4 == 0 && kXOut * (kXGroups - 1) + kXOut + 12 <= kVInP,
               "X-pass tasks read whole 16-byte words inside a tile row");
-static_assert(kQ * kVT * (kVTy / 4) == kVThreads, "one Y-pass task (4 outputs) per lane");
-static_assert(kVByP % 4 == 0 && 4 * (kVTy / 4 - 1) + 14 <= kVInY &&
+static_assert(kVT == 16 && kQ == 4 && kVTy / 4 == kVWaves,
+              "Y pass: a wave's lanes are 16 columns x 4 quantities, one 4-row group per wave");
+static_assert(kVByP % 4 == 0 && (kVByP / 4) % 2 == 1 && 4 * (kVTy / 4 - 1) + 14 <= kVInY &&
                   4 * (kVTy / 4 - 1) + 16 <= kVByP,
-              "Y-pass tasks read 16-byte words inside a column, of rows the X pass wrote");
-static_assert(kVT == 16 && kVTy % 8 == 0, "the transpose tile's bank layout assumes 16 columns");
+              "Y-pass tasks read 16-byte words inside a column, of rows the X pass wrote, "
+              "at an odd number of 16-byte words per column");
+static_assert(kVCq % 32 == 16, "the transpose tile's quantities sit 16 banks apart");
 
 struct VolParams {
   int D, H, W;          // volume extent
@@ -73,16 +88,22 @@ struct VolParams {
 };
 
 // This workgroup's share of (tile-column, output slice) work, as in the 2-D
-// kernels: a depth range of one tile-column, or whole tile-columns.
-__device__ __forceinline__ Share vol_share(const VolParams& p) {
+// kernels: a depth range of one tile-column, or whole tile-columns.  dir is
+// the direction the range is walked in: the odd ranges of a tile-column walk
+// down, so that neighbouring ranges reach the 10 input slices they share at
+// about the same time (both at their ends, or both at their starts), while
+// those are still in the cache.
+__device__ __forceinline__ Share vol_share(const VolParams& p, int& dir) {
   const int lb = logical_block();
   Share w;
+  dir = 1;
   if (p.parts > 1) {
     w.sc_begin = lb / p.parts;
     w.sc_end = w.sc_begin + 1;
     const int part = lb - (int)w.sc_begin * p.parts;
     w.row_begin = (int)((int64_t)part * p.out_d / p.parts);
     w.row_end = (int)((int64_t)(part + 1) * p.out_d / p.parts);
+    if (part & 1) dir = -1;
   } else {
     w.sc_begin = (int64_t)lb * p.per_block;
     w.sc_end = w.sc_begin + p.per_block < p.cols ? w.sc_begin + p.per_block : p.cols;
@@ -103,7 +124,20 @@ struct VolSeg {
 // One slice's input tile, held in registers between its loads and its LDS
 // store: each lane owns up to kVIters positions of the 42 x 26 tile (the
 // last iteration is partial).  Forward: x and y; backward: the 4 partials.
-constexpr int kVIters = (kVInY * kVIn + kVThreads - 1) / kVThreads;
+constexpr int kVIters = (kVInY * kVIn + kVThreads / 32 * kVHalf - 1) / (kVThreads / 32 * kVHalf);
+
+// The element of the row-major 42 x 26 tile that this lane stages in
+// iteration it, or kVInY * kVIn (none).  A half-wave takes 28 consecutive
+// elements (lanes 28 .. 31 idle): with the tile's 26-element rows at a
+// 28-word pitch they span at most 32 consecutive words, so the half-wave's
+// single-word LDS stores fall on 32 distinct banks.
+__device__ __forceinline__ int vol_stage_elem(int it) {
+  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int j = l % 32;
+  const int h = (it * kVWaves + w) * 2 + l / 32;
+  const int e = h * kVHalf + j;
+  return j < kVHalf && e < kVInY * kVIn ? e : kVInY * kVIn;
+}
 template <int MODE>
 struct VolPre {
   float v[kVIters][MODE == kBwd ? 4 : 2];
@@ -115,7 +149,7 @@ __device__ __forceinline__ void vol_tile_offsets(const VolParams& p, const VolSe
                                                  unsigned (&eo)[kVIters]) {
 #pragma unroll
   for (int it = 0; it < kVIters; ++it) {
-    const int t = threadIdx.x + it * kVThreads;
+    const int t = vol_stage_elem(it);
     const bool in_tile = t < kVInY * kVIn;
     const int tt = in_tile ? t : 0;
     const int r = tt / kVIn, c = tt - r * kVIn;
@@ -151,22 +185,23 @@ __device__ __forceinline__ void vol_load(const VolParams& p, const VolSeg& s, in
 
 // Store a loaded tile into LDS as the four quantities to be blurred.
 template <int MODE>
-__device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ][kVInY][kVInP]) {
+__device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ][kVAq]) {
 #pragma unroll
   for (int it = 0; it < kVIters; ++it) {
-    const int t = threadIdx.x + it * kVThreads;
+    const int t = vol_stage_elem(it);
     if (t < kVInY * kVIn) {
       const int r = t / kVIn, c = t - r * kVIn;
+      const int a = r * kVInP + c;
       if constexpr (MODE == kBwd) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) A[q][r][c] = pre.v[it][q];
+        for (int q = 0; q < kQ; ++q) A[q][a] = pre.v[it][q];
       } else {
         const float xv = pre.v[it][0], yv = pre.v[it][1];
         const float d = xv - yv;
-        A[0][r][c] = yv;
-        A[1][r][c] = d;
-        A[2][r][c] = d * d;
-        A[3][r][c] = (xv - kShift) * (yv - kShift);
+        A[0][a] = yv;
+        A[1][a] = d;
+        A[2][a] = d * d;
+        A[3][a] = (xv - kShift) * (yv - kShift);
       }
     }
   }
@@ -174,58 +209,54 @@ __device__ __forceinline__ void vol_store(const VolPre<MODE>& pre, float (&A)[kQ
 
 // X pass of one staged slice: 42 rows x 16 columns of partial sums, stored
 // column-major (Bx[q][column][row], columns padded to 44 words).  A task is
-// 4 adjacent outputs of one quantity in one row, formed from 16 columns read
-// as four 16-byte words; consecutive lanes take consecutive rows, so with
-// the 28-float row pitch any 8 (or 16) of them read distinct bank groups,
-// and their 4 single-word stores land on consecutive words.
+// 8 adjacent outputs of one quantity in one row, formed from 20 columns read
+// as five 16-byte words (the last two unused).  Tasks run (column group,
+// quantity, row) with rows padded to 48, one pass of the first six waves:
+// each 16 lanes take 16 consecutive rows of one quantity, whose 16-byte
+// reads (7 words of 16 bytes per row) fall on distinct bank groups, and
+// lanes 16 apart read the same bank group (16 rows, or the quantity stride
+// minus 32 rows, are whole multiples of 64 words); a column group starts a
+// wave.
 // kFwd: the forward's quantities, blurred by parts in every pass (all four
 // here, so that no wave splits between the two forms); otherwise plain.
-constexpr int kXTasks = kQ * (kVT / 4) * kVInY;
 template <bool kFwd>
-__device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVInY][kVInP],
+__device__ __forceinline__ void vol_xpass(const float (&A)[kQ][kVAq],
                                           float (&Bx)[kQ][kVT][kVByP]) {
+  const int t = threadIdx.x;
+  const int g = t / (kQ * kXRows);
+  const int rem = t - g * (kQ * kXRows);
+  const int q = rem / kXRows, r = rem - q * kXRows;
+  if (g < kXGroups && r < kVInY) {
+    const float* src = &A[q][r * kVInP + kXOut * g];
+    float v[kXOut + 12];
 #pragma unroll
-  for (int it = 0; it < (kXTasks + kVThreads - 1) / kVThreads; ++it) {
-    const int t = threadIdx.x + it * kVThreads;
-    if (t < kXTasks) {
-      const int q = t / ((kVT / 4) * kVInY);
-      const int rem = t - q * ((kVT / 4) * kVInY);
-      const int g = rem / kVInY, r = rem - g * kVInY;
-      const float* src = &A[q][r][4 * g];
-      float v[16];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
-        v[4 * k + 0] = f.x;
-        v[4 * k + 1] = f.y;
-        v[4 * k + 2] = f.z;
-        v[4 * k + 3] = f.w;
-      }
-      float o[4];
-      blur4<kFwd>(v, o);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) Bx[q][4 * g + u][r] = o[u];
+    for (int k = 0; k < (kXOut + 12) / 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(src + 4 * k);
+      v[4 * k + 0] = f.x;
+      v[4 * k + 1] = f.y;
+      v[4 * k + 2] = f.z;
+      v[4 * k + 3] = f.w;
     }
+    float o[kXOut];
+    blur_row<kFwd>(v, o);
+#pragma unroll
+    for (int u = 0; u < kXOut; ++u) Bx[q][kXOut * g + u][r] = o[u];
   }
 }
 
-// Row r of the transpose tile is stored at row r ^ bit 2 of r (rows 4..7,
-// 12..15, ... swap in pairs), so that with its 16-word rows both the Y pass's
-// stores (16 columns x rows 4g + u and 4g + 4 + u per half-wave) and the Z
-// pass's loads (16 columns x rows 2k and 2k + 1) fall on 32 distinct banks.
-__device__ __forceinline__ int vol_crow(int r) { return r ^ ((r >> 2) & 1); }
-
-// Y pass of one X-blurred slice.  A task (one per lane) is 4 outputs of one
-// quantity down one column, rows 4g .. 4g + 3, from the 14 words of that
-// column starting at row 4g, read as four 16-byte words (the last two words
-// unused): 4 reads per 4 outputs instead of 44.  Consecutive lanes take
-// consecutive columns, whose 44-word pitch puts any 8 of them on distinct
-// bank quads.  The outputs go to the transpose tile C[q][row][column].
+// Y pass of one X-blurred slice.  Wave w forms output rows 4w .. 4w + 3 of
+// every quantity: lane (q, column) reads the 14 words of its column starting
+// at row 4w as four 16-byte words (the last two words unused), 4 reads per 4
+// outputs.  The 16 columns of one quantity sit an odd number of 16-byte words
+// apart (44-word pitch), so a wave's 16-byte reads are free of bank
+// conflicts.  The outputs go to the transpose tile C[q][row * 16 + column],
+// whose quantities are 16 banks apart, so that each half-wave's stores (two
+// quantities, 16 columns) cover 32 distinct banks.
 template <bool kFwd>
 __device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
-                                          float (&C)[kQ][kVTy][kVT]) {
+                                          float (&C)[kQ][kVCq]) {
   const int t = threadIdx.x;
-  const int tx = t % kVT, g = (t / kVT) % (kVTy / 4), q = t / (kVT * (kVTy / 4));
+  const int tx = t % kVT, q = (t / kVT) % kQ, g = t / (kVT * kQ);
   const float* src = &Bx[q][tx][4 * g];
   float v[16];
 #pragma unroll
@@ -239,15 +270,14 @@ __device__ __forceinline__ void vol_ypass(const float (&Bx)[kQ][kVT][kVByP],
   float o[4];
   blur4<kFwd>(v, o);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) C[q][vol_crow(4 * g + u)][tx] = o[u];
+  for (int u = 0; u < 4; ++u) C[q][(4 * g + u) * kVT + tx] = o[u];
 }
 
 // The four XY-blurred quantities at this lane's (i, j), from the transpose
-// tile the Y pass wrote.
-__device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVTy][kVT], float (&a)[kQ]) {
-  const int ty = threadIdx.x / kVT, tx = threadIdx.x % kVT;
+// tile the Y pass wrote (a half-wave reads two 16-word rows: 32 banks).
+__device__ __forceinline__ void vol_ytake(const float (&C)[kQ][kVCq], float (&a)[kQ]) {
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) a[q] = C[q][vol_crow(ty)][tx];
+  for (int q = 0; q < kQ; ++q) a[q] = C[q][threadIdx.x];
 }
 
 // Z pass as running sums: acc[c] holds the partial sum, over the slices seen
@@ -430,15 +460,16 @@ __device__ __forceinline__ void vol_consume(const VolParams& p, const VolSeg& s,
 
 template <int MODE, bool kNt, int T>
 __device__ __forceinline__ void vol_body(const VolParams& p) {
-  __shared__ __align__(16) float A[2][kQ][kVInY][kVInP];
+  __shared__ __align__(16) float A[2][kQ][kVAq];
   __shared__ __align__(16) float Bx[2][kQ][kVT][kVByP];
-  __shared__ float C[2][kQ][kVTy][kVT];
+  __shared__ float C[2][kQ][kVCq];
   __shared__ double red[kVWaves];
   constexpr unsigned kEb = img_bytes<T>();
 
   float dl = 0.0f;
   if constexpr (MODE == kBwd) dl = *p.dloss;
-  const Share w = vol_share(p);
+  int dir;
+  const Share w = vol_share(p, dir);
   double acc = 0.0;
   for (int64_t sc = w.sc_begin; sc < w.sc_end; ++sc) {
     VolSeg s;
@@ -469,8 +500,10 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
     }
 
     // Input slices kin0 .. kin0 + nsl - 1 pass through the lane's running
-    // sums; the first 10 only start them, and slice kin0 + 10 + n completes
-    // output slice k0 + n.  Four stages per slice, one step apart, each
+    // sums, upwards (dir 1) or downwards (dir -1, the taps are symmetric);
+    // the first 10 only start them, and the (10 + n)-th completes the n-th
+    // output slice of the range in the same direction.  Four stages per
+    // slice, one step apart, each
     // step ending in the only barrier: in step j the tile of slice j goes
     // into A[j & 1] (its loads were issued in step j - 1), slice j - 1 is
     // blurred in X from A[(j - 1) & 1] into Bx[(j - 1) & 1], slice j - 2 in
@@ -485,16 +518,18 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       for (int q = 0; q < kQ; ++q) acc_z[k][q] = 0.0f;
     const int kin0 = s.k0 - p.off;
     const int nsl = 10 + s.nk;
+    const int kin_first = dir > 0 ? kin0 : kin0 + nsl - 1;
+    const int kout_first = dir > 0 ? s.k0 : s.k0 + s.nk - 1;
     unsigned eo[kVIters];
     vol_tile_offsets(p, s, eo);
     const unsigned oo = vol_out_pos(p, s);
     VolPre<MODE> pre;
-    vol_load<MODE, T>(p, s, kin0, eo, pre);
+    vol_load<MODE, T>(p, s, kin_first, eo, pre);
     float xy[2] = {0.0f, 0.0f};
     for (int j = 0; j < nsl + 3; ++j) {
       if (j < nsl) {
         vol_store<MODE>(pre, A[j & 1]);
-        vol_load<MODE, T>(p, s, kin0 + j + 1, eo, pre);
+        vol_load<MODE, T>(p, s, kin_first + dir * (j + 1), eo, pre);
       }
       if (j >= 1 && j <= nsl) vol_xpass<MODE != kBwd>(A[(j - 1) & 1], Bx[(j - 1) & 1]);
       if (j >= 2 && j <= nsl + 1) vol_ypass<MODE != kBwd>(Bx[j & 1], C[j & 1]);
@@ -504,11 +539,12 @@ __device__ __forceinline__ void vol_body(const VolParams& p) {
       if (j >= 3) vol_ytake(C[(j - 1) & 1], a);
       if constexpr (MODE == kBwd) vol_zpass(acc_z, a);
       else vol_zpass_by_parts(acc_z, a, zprev);
-      const int n = j - 13;  // output slice k0 + n, once its 11 slices are in
-      if (n >= 0) vol_consume<MODE, kNt, T>(p, s, s.k0 + n, oo, acc_z[10], xy, dl, acc);
+      const int n = j - 13;  // the range's n-th output slice, once its 11 slices are in
+      if (n >= 0)
+        vol_consume<MODE, kNt, T>(p, s, kout_first + dir * n, oo, acc_z[10], xy, dl, acc);
       // the chain rule's x, y for the next step's output slice
       if constexpr (MODE == kBwd) {
-        if (j >= 12 && j < nsl + 2) vol_load_xy<T>(p, s, s.k0 + j - 12, oo, xy);
+        if (j >= 12 && j < nsl + 2) vol_load_xy<T>(p, s, kout_first + dir * (j - 12), oo, xy);
       }
       __syncthreads();
     }
