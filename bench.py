@@ -828,7 +828,7 @@ def main():
         summarize_profile(args.workload, args.dtype, outdir)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by image planes with one scalar all-reduce, which is not built",
               file=sys.stderr)
         sys.exit(2)
