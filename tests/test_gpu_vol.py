@@ -63,11 +63,12 @@ def test_volume_parity(shape, padding):
     say(f"  loss gpu {gl:.9f} oracle {ol:.9f}; grad err/max {r1:.2e} {r2:.2e}")
 
 
-def test_volume_workload_loss_and_sampled_grads():
+def test_volume_workload_loss_and_grads():
     """The 2 x 3 x 96^3 volumes of the page's 3-D example (same padding): the
-    whole loss against the oracle's whole loss, gradients at sampled voxels
-    (every corner of several volumes, tile and window borders, random
-    interior points), each computed one by one by the oracle."""
+    whole loss and both whole gradients against the oracle's, every volume's
+    gradients element by element; and gradients at sampled voxels (every
+    corner of several volumes, tile and window borders, random interior
+    points), each computed one by one by the oracle's single-voxel routine."""
     import torch
 
     w = WORKLOADS["vol-96"]
@@ -96,10 +97,16 @@ def test_volume_workload_loss_and_sampled_grads():
         o1[k], o2[k] = oracle.sample_grad3(x[n, c], y[n, c], w.padding, M, dloss, t, u, v)
     check_grad(s1, o1, "vol-96 grad_vol1 samples")
     check_grad(s2, o2, "vol-96 grad_vol2 samples")
-    say("  oracle whole loss")
-    ol, _, _ = oracle.ssim3_loss(x, y, w.padding, grads=False)
+    say("  oracle whole loss and gradients")
+    ol, og1, og2 = oracle.ssim3_loss(x, y, w.padding, dloss=dloss)
     check_loss(gl, ol, "vol-96")
-    say(f"  loss gpu {gl:.9f} oracle {ol:.9f}")
+    g1h, g2h = g1.cpu().numpy(), g2.cpu().numpy()
+    worst = 0.0
+    for n in range(N):
+        for c in range(C):
+            worst = max(worst, check_grad(g1h[n, c], og1[n, c], f"vol-96 ({n},{c}) grad_vol1"),
+                        check_grad(g2h[n, c], og2[n, c], f"vol-96 ({n},{c}) grad_vol2"))
+    say(f"  loss gpu {gl:.9f} oracle {ol:.9f}; worst grad err/max per volume {worst:.2e}")
 
 
 def test_volume_random_shapes():
