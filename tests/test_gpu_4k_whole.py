@@ -86,3 +86,62 @@ def test_4k_batch8_whole_gradients_every_path():
         check_loss(gl, ol, f"{p} loss")
         say(f"  {p}: loss {gl:.9f} (oracle {ol:.9f}); worst grad err/max "
             f"{worst[p][0]:.2e} {worst[p][1]:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+def test_4k_batch8_half_images_whole_gradients(dtype):
+    """The same batch stored as half-precision images (the kernels that
+    stream 16-bit tensors of this size): the one-launch and recomputing steps,
+    both gradients, every element against the oracle on the half values, with
+    the storage rounding in the bar (tests/test_gpu_half.py).  The upstream
+    gradient is a power of two that brings the largest gradient near 1 (loss
+    scaling; float16 would flush these gradients, of order 1/M, to zero)."""
+    import torch
+
+    import ssim_loss_amd as S
+    from test_gpu_half import _check_half_grad, _loss_scale, _round
+
+    name = "4k-batch8"
+    w = WORKLOADS[name]
+    say(f"[whole-{dtype}] {name} {w.shape} generating inputs")
+    x, y = make_workload(name)
+    xh, yh = _round(x, dtype), _round(y, dtype)
+    del x, y
+    N = xh.shape[0]
+    say("  oracle image 0 (for the loss scale)")
+    first = oracle.ssim_loss(xh[:1], yh[:1], w.padding, dloss=1.0 / N)
+    scale = _loss_scale((first[1], first[2]))
+    dev = torch.device("cuda")
+    td = getattr(torch, dtype)
+    t1 = torch.from_numpy(xh).to(dev).to(td)
+    t2 = torch.from_numpy(yh).to(dev).to(td)
+    paths = {}
+    say(f"  one launch (dloss {scale:g})")
+    loss, g1, g2 = S.loss_and_grad(t1, t2, w.padding, scale, True, True)
+    torch.cuda.synchronize()
+    paths["one-launch"] = (float(loss.item()), g1, g2)
+    say("  inference forward + recomputing backward")
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    S.ssim_forward(t1, t2, w.padding, loss, None, S.workspace_for(dev))
+    dl = torch.tensor(scale, dtype=torch.float32, device=dev)
+    g1, g2 = torch.empty_like(t1), torch.empty_like(t2)
+    S.ssim_backward_recompute(dl, t1, t2, w.padding, g1, g2)
+    torch.cuda.synchronize()
+    paths["recompute"] = (float(loss.item()), g1, g2)
+
+    losses = []
+    worst = {p: 0.0 for p in paths}
+    for n in range(N):
+        say(f"  oracle image {n}")
+        ol, og1, og2 = first if n == 0 else oracle.ssim_loss(xh[n:n + 1], yh[n:n + 1], w.padding,
+                                                             dloss=1.0 / N)
+        losses.append(ol)
+        og1, og2 = og1 * scale, og2 * scale
+        for p, (_, g1, g2) in paths.items():
+            worst[p] = max(worst[p],
+                           _check_half_grad(g1[n:n + 1], og1, dtype, f"{p} image {n} grad_img1"),
+                           _check_half_grad(g2[n:n + 1], og2, dtype, f"{p} image {n} grad_img2"))
+    ol = float(np.mean(losses))
+    for p, (gl, _, _) in paths.items():
+        check_loss(gl, ol, f"{p} loss")
+        say(f"  {p}: loss {gl:.9f} (oracle {ol:.9f}); worst grad err/max {worst[p]:.2e}")
