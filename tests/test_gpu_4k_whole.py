@@ -91,8 +91,9 @@ def test_4k_batch8_whole_gradients_every_path():
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
 def test_4k_batch8_half_images_whole_gradients(dtype):
     """The same batch stored as half-precision images (the kernels that
-    stream 16-bit tensors of this size): the one-launch and recomputing steps,
-    both gradients, every element against the oracle on the half values, with
+    stream 16-bit tensors of this size): the one-launch and recomputing steps
+    (both gradients) and the cached reference (grad_img1), every element
+    against the oracle on the half values, with
     the storage rounding in the bar (tests/test_gpu_half.py).  The upstream
     gradient is a power of two that brings the largest gradient near 1 (loss
     scaling; float16 would flush these gradients, of order 1/M, to zero)."""
@@ -128,6 +129,12 @@ def test_4k_batch8_half_images_whole_gradients(dtype):
     S.ssim_backward_recompute(dl, t1, t2, w.padding, g1, g2)
     torch.cuda.synchronize()
     paths["recompute"] = (float(loss.item()), g1, g2)
+    say("  cached reference")
+    ref = S.reference_stats(t2, w.padding)
+    loss, g1 = S.loss_and_grad_ref(t1, t2, ref, w.padding, scale, True)
+    torch.cuda.synchronize()
+    paths["reference"] = (float(loss.item()), g1, None)
+    del ref
 
     losses = []
     worst = {p: 0.0 for p in paths}
@@ -139,8 +146,10 @@ def test_4k_batch8_half_images_whole_gradients(dtype):
         og1, og2 = og1 * scale, og2 * scale
         for p, (_, g1, g2) in paths.items():
             worst[p] = max(worst[p],
-                           _check_half_grad(g1[n:n + 1], og1, dtype, f"{p} image {n} grad_img1"),
-                           _check_half_grad(g2[n:n + 1], og2, dtype, f"{p} image {n} grad_img2"))
+                           _check_half_grad(g1[n:n + 1], og1, dtype, f"{p} image {n} grad_img1"))
+            if g2 is not None:
+                worst[p] = max(worst[p], _check_half_grad(g2[n:n + 1], og2, dtype,
+                                                          f"{p} image {n} grad_img2"))
     ol = float(np.mean(losses))
     for p, (gl, _, _) in paths.items():
         check_loss(gl, ol, f"{p} loss")
