@@ -185,6 +185,22 @@ def test_objects_and_dark_fields(kind, noise, padding):
             _flat_case(a, b, padding, kind)
 
 
+@pytest.mark.parametrize("padding", ["valid", "same"])
+@pytest.mark.parametrize("lo,hi", [(-0.5, 1.5), (-1.0, 2.0), (0.0, 4.0), (0.0, 255.0)])
+def test_values_outside_the_unit_range(lo, hi, padding):
+    """The pages take images in [0, 1], and C1 and C2 assume that range, but
+    the formula is defined for any values: uniform images on [lo, hi] against
+    a copy with noise of 5% of the range, unclamped, at the contract's bars
+    (the kernels' shift by 1/2 is exact arithmetic, not an assumption on the
+    range)."""
+    rng = np.random.default_rng(5)
+    x = rng.uniform(lo, hi, (1, 2, 120, 150))
+    y = (x + rng.normal(0.0, 0.05 * (hi - lo), x.shape)).astype(np.float32)
+    x = x.astype(np.float32)
+    say(f"[range] [{lo}, {hi}] {padding}")
+    _flat_case(x, y, padding, f"range [{lo}, {hi}]")
+
+
 def test_nullable_gradients_and_dloss_scaling():
     say("[api] grad_img1 / grad_img2 = NULL, dloss scaling")
     x, y = make_pair((2, 3, 70, 90), "uniform", 0.1, seed=11)
