@@ -65,3 +65,31 @@ def test_noalloc_repeated_calls_leave_the_accumulator_clear():
     torch.cuda.synchronize()
     vals = {float(l.item()) for l in losses}
     assert len(vals) == 1, vals
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+def test_noalloc_half_images_match_loss_and_grad(dtype):
+    """Half-precision images and gradients: the same bits as
+    ssim_loss_and_grad, on two calls in a row (the second smaller)."""
+    import torch
+
+    import ssim_loss_amd as S
+
+    dev = torch.device("cuda")
+    ws = S.workspace_for(dev)
+    td = getattr(torch, dtype)
+    for shape, padding, seed in (((1, 3, 260, 400), "same", 21), ((1, 1, 40, 60), "valid", 22)):
+        say("noalloc", dtype, shape, padding, seed)
+        x, y = _pair(shape, seed)
+        t1 = torch.from_numpy(x).to(dev).to(td)
+        t2 = torch.from_numpy(y).to(dev).to(td)
+        dl = torch.tensor(64.0, dtype=torch.float32, device=dev)
+        l_ref, l_na = (torch.empty((), dtype=torch.float32, device=dev) for _ in range(2))
+        g_ref = (torch.empty_like(t1), torch.empty_like(t2))
+        g_na = (torch.full_like(t1, float("nan")), torch.full_like(t2, float("nan")))
+        S.ssim_loss_and_grad(t1, t2, padding, dl, l_ref, ws, *g_ref)
+        S.ssim_loss_and_grad_noalloc(t1, t2, padding, dl, l_na, *g_na)
+        torch.cuda.synchronize()
+        assert l_na.item() == l_ref.item(), (l_na.item(), l_ref.item())
+        for a, b in zip(g_na, g_ref):
+            assert torch.equal(a, b)
