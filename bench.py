@@ -11,6 +11,8 @@ current stream:
               ssim_backward_recompute (both gradients, no maps)
   one-pass-ref : ssim_loss_and_grad_ref (a fixed reference whose statistics
               were cached outside the step; grad_img1 only)
+  one-pass-x : ssim_loss_and_grad with grad_img2 NULL (a kernel that forms
+              grad_img1 alone, as when only the render is differentiable)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--dtype float32|float16|bfloat16] [--design NAME]
@@ -55,12 +57,13 @@ def parse():
     ap.add_argument("--dtype", default="float32", choices=["float32", "float16", "bfloat16"],
                     help="storage type of images and gradients (arithmetic is fp32)")
     ap.add_argument("--design", default="one-pass",
-                    choices=["saved", "recompute", "one-pass", "one-pass-ref"],
+                    choices=["saved", "recompute", "one-pass", "one-pass-ref", "one-pass-x"],
                     help="saved: forward saves the statistics, backward reads them; "
                          "recompute: loss-only forward, backward recomputes the statistics; "
                          "one-pass: loss and gradients in one launch; "
                          "one-pass-ref: the same with the reference's statistics cached and "
-                         "only the first image's gradient")
+                         "only the first image's gradient; "
+                         "one-pass-x: one launch forming the first image's gradient alone")
     ap.add_argument("--all-kernels", action=argparse.BooleanOptionalAction, default=True,
                     help="after the timed steps, also time the kernels of the other designs "
                          "(reported under 'designs'; on by default)")
@@ -133,7 +136,8 @@ def algorithmic_bytes(shape, padding, eb=4):
     both gradients (2 eb per element).  The recomputing kernels read x, y and
     write both gradients (4 eb per element); the inference forward reads x, y.
     With a cached reference: x, y and the cached map (4 B per map entry) in,
-    grad_x out; forming that map reads y and writes it."""
+    grad_x out; forming that map reads y and writes it.  One launch forming
+    grad_x alone: x, y in, grad_x out (3 eb per element)."""
     N, C, H, W = shape
     Ho, Wo = (H - 10, W - 10) if padding == "valid" else (H, W)
     e_in = N * C * H * W
@@ -144,6 +148,7 @@ def algorithmic_bytes(shape, padding, eb=4):
             "ssim_backward_recompute": 4 * eb * e_in,
             "ssim_loss_and_grad": 4 * eb * e_in,
             "ssim_loss_and_grad_ref": 3 * eb * e_in + 4 * e_out,
+            "ssim_loss_and_grad(grad_x)": 3 * eb * e_in,
             "ssim_reference_stats": eb * e_in + 4 * e_out}
 
 
@@ -166,9 +171,12 @@ def algorithmic_flops(shape, padding):
     recompute = 5 * e_in + (blur + 17 + 25) * e_out + (blur + 13) * e_in
     blur3 = 3 * 2 * 21  # three quantities
     ref_step = 5 * e_in + (blur3 + 17 + 5 + 25) * e_out + (blur3 + 7) * e_in
+    # grad_x alone: all four quantities forward, three partials backward
+    x_step = 5 * e_in + (blur + 17 + 5 + 25) * e_out + (blur3 + 7) * e_in
     return {"ssim_forward": fwd, "ssim_forward(inference)": fwd,
             "ssim_backward": bwd_from_stats, "ssim_backward_recompute": recompute,
-            "ssim_loss_and_grad": recompute + 5 * e_out, "ssim_loss_and_grad_ref": ref_step}
+            "ssim_loss_and_grad": recompute + 5 * e_out, "ssim_loss_and_grad_ref": ref_step,
+            "ssim_loss_and_grad(grad_x)": x_step}
 
 
 def cpu_model():
@@ -487,6 +495,10 @@ def autograd_record(t1, t2, padding, reps):
 # type, entry point).  Stream and unaligned variants count for their entry.
 KERNEL_ENTRY = [
     ("ssim_loss_grad_ref", "ssim_loss_and_grad_ref"),
+    ("ssim_loss_grad_x", "ssim_loss_and_grad(grad_x)"),
+    ("ssim_loss_grad_y", "ssim_loss_and_grad(grad_y)"),
+    ("ssim_bwd_recompute_x", "ssim_backward_recompute(grad_x)"),
+    ("ssim_bwd_recompute_y", "ssim_backward_recompute(grad_y)"),
     ("ssim_loss_grad", "ssim_loss_and_grad"),
     ("ssim_bwd_recompute", "ssim_backward_recompute"),
     ("ssim_bwd", "ssim_backward"),
@@ -814,6 +826,8 @@ DESIGNS = {
     # a fixed reference with its statistics cached (computed once, outside
     # the step), only the first image's gradient
     "one-pass-ref": ("ssim_loss_and_grad_ref",),
+    # only the first image's gradient (the second pointer NULL)
+    "one-pass-x": ("ssim_loss_and_grad(grad_x)",),
 }
 
 
@@ -869,6 +883,8 @@ def main():
             lambda: S.ssim_loss_and_grad(t1, t2, w.padding, dloss, loss, ws, g1, g2),
         "ssim_loss_and_grad_ref":
             lambda: S.ssim_loss_and_grad_ref(t1, t2, ref, w.padding, dloss, loss, ws, g1),
+        "ssim_loss_and_grad(grad_x)":
+            lambda: S.ssim_loss_and_grad(t1, t2, w.padding, dloss, loss, ws, g1, None),
     }
     step_launches = [launches[k] for k in DESIGNS[args.design]]
 

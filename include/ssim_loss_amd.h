@@ -176,7 +176,11 @@ int ssim_backward_typed(const float* dloss, const void* img1, const void* img2, 
  *   dloss        : device fp32 scalar, the upstream gradient of the loss
  *   img1, img2   : device images of `dtype` (inputs)
  *   dtype, N..padding : as for ssim_forward_typed
- *   grad_img1/2  : device outputs of `dtype`, or NULL to skip (both NULL: no-op)
+ *   grad_img1/2  : device outputs of `dtype`, or NULL to skip (both NULL: no-op);
+ *                  with exactly one NULL (and 16-byte aligned images, W a
+ *                  multiple of 4) a kernel runs that forms the other gradient
+ *                  alone, bit for bit the same, skipping the missing one's
+ *                  partial and adjoint blur
  *   stream       : hipStream_t (NULL = default stream) */
 int ssim_backward_recompute(const float* dloss, const void* img1, const void* img2, int dtype,
                             int64_t N, int64_t C, int64_t H, int64_t W, int padding,
@@ -195,7 +199,10 @@ int ssim_backward_recompute(const float* dloss, const void* img1, const void* im
  *   loss         : device fp32 scalar (output; required)
  *   workspace    : as for ssim_forward (the same rules: zeroed once, not
  *                  shared by calls that may overlap)
- *   grad_img1/2  : device outputs of `dtype`, or NULL to skip
+ *   grad_img1/2  : device outputs of `dtype`, or NULL to skip; with exactly one
+ *                  NULL (and 16-byte aligned images, W a multiple of 4) a
+ *                  kernel runs that forms the other gradient alone, bit for
+ *                  bit the same
  *   stream       : hipStream_t (NULL = default stream)
  * Deterministic, like ssim_forward; the loss equals ssim_forward's up to the
  * rounding of the summation (the two kernels split the map differently). */

@@ -429,6 +429,14 @@ int recompute_impl(const float* dloss, const void* img1, const void* img2, int d
   const bool stream_st = 4 * s.img_bytes > kStreamBytes;
   int which = loss ? (!vec ? kKLossGradUnaligned : stream_st ? kKLossGradStream : kKLossGrad)
                    : (!vec ? kKRecompUnaligned : stream_st ? kKRecompStream : kKRecomp);
+  // one gradient wanted: the kernels that skip the other's partial and blur
+  if (vec && (grad_img1 == nullptr) != (grad_img2 == nullptr)) {
+    const bool x = grad_img1 != nullptr;
+    which = loss ? (x ? (stream_st ? kKLossGradXStream : kKLossGradX)
+                      : (stream_st ? kKLossGradYStream : kKLossGradY))
+                 : (x ? (stream_st ? kKRecompXStream : kKRecompX)
+                      : (stream_st ? kKRecompYStream : kKRecompY));
+  }
   if (ref) {
     which = !vec ? kKLossGradRefUnaligned : stream_st ? kKLossGradRefStream : kKLossGradRef;
     p.maps = const_cast<float*>(ref);

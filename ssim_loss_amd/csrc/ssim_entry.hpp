@@ -30,6 +30,14 @@ enum KernelKind {
   kKLossGradRef,       // loss and grad_x in one pass, with cached reference statistics
   kKLossGradRefStream,
   kKLossGradRefUnaligned,
+  kKRecompX,           // the recomputing backward and the one-pass step forming
+  kKRecompXStream,     // grad_x alone or grad_y alone (the other pointer NULL);
+  kKRecompY,           // the unaligned case uses the both-gradient kernels
+  kKRecompYStream,
+  kKLossGradX,
+  kKLossGradXStream,
+  kKLossGradY,
+  kKLossGradYStream,
   kKRefStats,          // the cached reference statistics of an image
   kKVolFwdInfer,       // volumes: forward, loss only
   kKVolFwdTrain,       // volumes: forward, loss + saved partials
@@ -37,7 +45,7 @@ enum KernelKind {
   kKinds
 };
 __host__ __device__ constexpr int kind_threads(int k) {
-  return (k >= kKRecomp && k <= kKLossGradRefUnaligned) ? kFThreads
+  return (k >= kKRecomp && k <= kKLossGradYStream) ? kFThreads
          : k >= kKVolFwdInfer                           ? kVThreads
                                                         : kThreads;
 }
@@ -94,6 +102,22 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
                 (ssim_dev::fused_body<true, true, true, T, true>))                         \
   SSIM_FKERNEL_(ssim_loss_grad_ref_unaligned##NAME##kernel,                                \
                 (ssim_dev::fused_body<true, false, false, T, true>))                       \
+  SSIM_FKERNEL_(ssim_bwd_recompute_x##NAME##kernel,                                         \
+                (ssim_dev::fused_body<false, true, false, T, false, ssim_dev::kOnlyX>))     \
+  SSIM_FKERNEL_(ssim_bwd_recompute_x_stream##NAME##kernel,                                  \
+                (ssim_dev::fused_body<false, true, true, T, false, ssim_dev::kOnlyX>))      \
+  SSIM_FKERNEL_(ssim_bwd_recompute_y##NAME##kernel,                                         \
+                (ssim_dev::fused_body<false, true, false, T, false, ssim_dev::kOnlyY>))     \
+  SSIM_FKERNEL_(ssim_bwd_recompute_y_stream##NAME##kernel,                                  \
+                (ssim_dev::fused_body<false, true, true, T, false, ssim_dev::kOnlyY>))      \
+  SSIM_FKERNEL_(ssim_loss_grad_x##NAME##kernel,                                             \
+                (ssim_dev::fused_body<true, true, false, T, false, ssim_dev::kOnlyX>))      \
+  SSIM_FKERNEL_(ssim_loss_grad_x_stream##NAME##kernel,                                      \
+                (ssim_dev::fused_body<true, true, true, T, false, ssim_dev::kOnlyX>))       \
+  SSIM_FKERNEL_(ssim_loss_grad_y##NAME##kernel,                                             \
+                (ssim_dev::fused_body<true, true, false, T, false, ssim_dev::kOnlyY>))      \
+  SSIM_FKERNEL_(ssim_loss_grad_y_stream##NAME##kernel,                                      \
+                (ssim_dev::fused_body<true, true, true, T, false, ssim_dev::kOnlyY>))       \
   SSIM_KERNEL_(ssim_ref_stats##NAME##kernel,                                               \
                (ssim_dev::strip_body<ssim_dev::kRef, false, false, T>))                    \
   SSIM_VKERNEL_(ssim3d_fwd_infer##NAME##kernel, 4,                                         \
@@ -119,6 +143,14 @@ __host__ __device__ constexpr bool kind_is_volume(int k) { return k >= kKVolFwdI
         (const void*)ssim_loss_grad_ref##NAME##kernel,                                     \
         (const void*)ssim_loss_grad_ref_stream##NAME##kernel,                              \
         (const void*)ssim_loss_grad_ref_unaligned##NAME##kernel,                           \
+        (const void*)ssim_bwd_recompute_x##NAME##kernel,                                   \
+        (const void*)ssim_bwd_recompute_x_stream##NAME##kernel,                            \
+        (const void*)ssim_bwd_recompute_y##NAME##kernel,                                   \
+        (const void*)ssim_bwd_recompute_y_stream##NAME##kernel,                            \
+        (const void*)ssim_loss_grad_x##NAME##kernel,                                       \
+        (const void*)ssim_loss_grad_x_stream##NAME##kernel,                                \
+        (const void*)ssim_loss_grad_y##NAME##kernel,                                       \
+        (const void*)ssim_loss_grad_y_stream##NAME##kernel,                                \
         (const void*)ssim_ref_stats##NAME##kernel,                                         \
         (const void*)ssim3d_fwd_infer##NAME##kernel,                                       \
         (const void*)ssim3d_fwd_train##NAME##kernel,                                       \

@@ -195,20 +195,30 @@ __device__ __forceinline__ void row_pass(const float* row0, int c, float (&o)[kQ
   }
 }
 
+// Which gradients a kernel forms: kBoth, or one of them (the other pointer
+// is NULL); a cached reference implies grad_x alone.  The loss partial, and
+// the adjoint blur, that only the missing gradient needs are skipped:
+// grad_x = B^T m0 + y' B^T m3 + d B^T m2 never uses m1, and grad_y = B^T m1 +
+// x' B^T m3 - d B^T m2 never uses m0.
+constexpr int kBoth = -1, kOnlyX = 0, kOnlyY = 1;
+__host__ __device__ constexpr int unused_partial(bool ref, int grads) {
+  return (ref || grads == kOnlyX) ? 1 : grads == kOnlyY ? 0 : -1;
+}
+
 // Stage 1 of batch t (PH = t mod 3): the column pass of image rows u0 + 4t
 // .. +3 into the tile, then the row pass of tile row `wave` -> SSIM terms,
 // loss and partials, written back over that row.  Two barriers.
-template <bool kLoss, int T, int PH, bool kRef>
+template <bool kLoss, int T, int PH, bool kRef, int kGrads>
 __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              float (&xyr)[kXYRing][2][kFTileW],
                                              float (&ring)[kRing][kQ], float (&prev)[kByParts],
                                              float (&pre)[kRows][2], unsigned mk, int t, int buf,
                                              int col, int wave, int lane, double& acc) {
-  // with a cached reference, B(y) (quantity 0) is read, not blurred, and the
-  // partial for mu_y (1), which feeds grad_y alone, is not passed on
+  // with a cached reference, B(y) (quantity 0) is read, not blurred; the
+  // partial that only a missing gradient needs is not passed on
   constexpr int kSkip = kRef ? 0 : -1;
-  constexpr int kSkipPart = kRef ? 1 : -1;
+  constexpr int kSkipPart = unused_partial(kRef, kGrads);
   const int i = s.i0 + 4 * t + wave;
   const bool irow = (unsigned)i < (unsigned)p.map_h;
   const int lr = lane < kFMapLanes ? lane : kFMapLanes - 1;
@@ -304,15 +314,16 @@ __device__ __forceinline__ void stage1_batch(const Params& p, const FSeg& s,
 // left in the tile (lane t owns map column jm0 + t; written back into the
 // same column), then the row pass of tile row `wave` and the chain rule for
 // gradient row u0 + 4t + wave - 10.  Two barriers.
-template <bool kVec, bool kNt, int T, int PH, bool kRef>
+template <bool kVec, bool kNt, int T, int PH, bool kRef, int kGrads>
 __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
                                              float (&tile)[2][kQ][kRows][kFTileW],
                                              const float (&xyr)[kXYRing][2][kFTileW],
                                              float (&ring)[kRing][kQ], int t, int buf, int col,
                                              int wave, int lane, float dl) {
-  // with a cached reference only grad_x is formed: m1 (which feeds grad_y
-  // alone) is neither blurred nor used
-  constexpr int kSkip = kRef ? 1 : -1;
+  // with a cached reference only grad_x is formed; the partial that only a
+  // missing gradient needs is neither blurred nor used
+  constexpr int kSkip = unused_partial(kRef, kGrads);
+  constexpr bool kG1 = kSkip != 0, kG2 = kSkip != 1;
   constexpr unsigned kEb = img_bytes<T>();
   // the gradient row this wave finishes; its x and y come from the row ring
   // that stage 1 filled (no second read of the images).  Stores are never
@@ -364,19 +375,20 @@ __device__ __forceinline__ void stage2_batch(const Params& p, const FSeg& s,
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float xs = xv[c] - kShift, ys = yv[c] - kShift, d = xv[c] - yv[c];
-      g1[c] = dl * __builtin_fmaf(d, o[2][c], __builtin_fmaf(ys, o[3][c], o[0][c]));
-      if constexpr (!kRef)
+      if constexpr (kG1)
+        g1[c] = dl * __builtin_fmaf(d, o[2][c], __builtin_fmaf(ys, o[3][c], o[0][c]));
+      if constexpr (kG2)
         g2[c] = dl * __builtin_fmaf(-d, o[2][c], __builtin_fmaf(xs, o[3][c], o[1][c]));
     }
   }
   if constexpr (kVec) {
-    st_img4<T, kNt>(s.out[0], gbase, g1);
-    if constexpr (!kRef) st_img4<T, kNt>(s.out[1], gbase, g2);
+    if constexpr (kG1) st_img4<T, kNt>(s.out[0], gbase, g1);
+    if constexpr (kG2) st_img4<T, kNt>(s.out[1], gbase, g2);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      st_img<T, kNt>(s.out[0], goff[c], g1[c]);
-      if constexpr (!kRef) st_img<T, kNt>(s.out[1], goff[c], g2[c]);
+      if constexpr (kG1) st_img<T, kNt>(s.out[0], goff[c], g1[c]);
+      if constexpr (kG2) st_img<T, kNt>(s.out[1], goff[c], g2[c]);
     }
   }
   __syncthreads();
@@ -488,7 +500,8 @@ __device__ __forceinline__ int segment_batches(const FSeg& s) {
 // through the last), so the two loops meet at every barrier.
 // kRef: B(y) comes from a cached map (p.maps, the layout the
 // reference-statistics kernel writes) and only grad_x is formed.
-template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false>
+// kGrads: both gradients, or grad_x (kOnlyX) or grad_y (kOnlyY) alone.
+template <bool kLoss, bool kVec, bool kNt, int T, bool kRef = false, int kGrads = kBoth>
 __device__ __forceinline__ void fused_body(const Params& p) {
   __shared__ float tile[2][kQ][kRows][kFTileW];
   __shared__ float xyr[kXYRing][2][kFTileW];
@@ -545,15 +558,15 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       }
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage1_batch<kLoss, T, 0, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 0, kRef, kGrads>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 1, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 1, kRef, kGrads>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         if (++t >= nb) break;
-        stage1_batch<kLoss, T, 2, kRef>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
+        stage1_batch<kLoss, T, 2, kRef, kGrads>(p, s, tile, xyr, ring, prev, pre, mk, t, (gb + t) & 1, col, wave_id,
                                           lane,
                                           acc);
         ++t;
@@ -581,11 +594,11 @@ __device__ __forceinline__ void fused_body(const Params& p) {
       __syncthreads();
       for (int t = 0;;) {
         if (t >= nb) break;
-        stage2_batch<kVec, kNt, T, 0, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 0, kRef, kGrads>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 1, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 1, kRef, kGrads>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         if (++t >= nb) break;
-        stage2_batch<kVec, kNt, T, 2, kRef>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
+        stage2_batch<kVec, kNt, T, 2, kRef, kGrads>(p, s, tile, xyr, ring, t, (gb + t) & 1, col, wave, lane, dl);
         ++t;
       }
       gb += nb;

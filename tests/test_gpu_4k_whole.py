@@ -61,6 +61,17 @@ def test_4k_batch8_whole_gradients_every_path():
     torch.cuda.synchronize()
     paths["one-launch"] = (float(loss.item()), g1, g2)
 
+    say("  one launch, grad_x alone (grad_img2 NULL)")
+    loss, g1, _ = S.loss_and_grad(t1, t2, w.padding, dloss, True, False)
+    torch.cuda.synchronize()
+    paths["one-launch grad_x"] = (float(loss.item()), g1, None)
+
+    say("  recompute, grad_y alone (grad_img1 NULL)")
+    g2 = torch.empty_like(t2)
+    S.ssim_backward_recompute(dl, t1, t2, w.padding, None, g2)
+    torch.cuda.synchronize()
+    paths["recompute grad_y"] = (paths["recompute"][0], None, g2)
+
     say("  cached reference: ssim_reference_stats + ssim_loss_and_grad_ref")
     ref = S.reference_stats(t2, w.padding)
     loss, g1 = S.loss_and_grad_ref(t1, t2, ref, w.padding, dloss, True)
@@ -75,8 +86,9 @@ def test_4k_batch8_whole_gradients_every_path():
         ol, og1, og2 = oracle.ssim_loss(x[n:n + 1], y[n:n + 1], w.padding, dloss=dloss / N)
         losses.append(ol)
         for p, (_, g1, g2) in paths.items():
-            r = check_grad(g1[n:n + 1].cpu().numpy(), og1, f"{p} image {n} grad_img1")
-            worst[p][0] = max(worst[p][0], r)
+            if g1 is not None:
+                r = check_grad(g1[n:n + 1].cpu().numpy(), og1, f"{p} image {n} grad_img1")
+                worst[p][0] = max(worst[p][0], r)
             if g2 is not None:
                 r = check_grad(g2[n:n + 1].cpu().numpy(), og2, f"{p} image {n} grad_img2")
                 worst[p][1] = max(worst[p][1], r)

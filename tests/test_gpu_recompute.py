@@ -255,3 +255,24 @@ def test_recompute_autograd_and_workspace_interleaving():
         check_grad(g1.cpu().numpy(), og1, "one-pass grad_img1")
         lf = S.ssim_loss(t1.detach(), t2.detach(), "same", train=False)
         check_loss(float(lf.item()), ol, f"forward {k}")
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "float16"])
+@pytest.mark.parametrize("path", list(RUNNERS))
+def test_one_gradient_kernels_match_the_two_gradient_kernel(path, dtype):
+    """With one gradient pointer NULL the step runs a kernel that skips the
+    other gradient's partial and adjoint blur.  The gradient it forms, and the
+    loss, are bit for bit those of the kernel that forms both (the same
+    arithmetic in the same order), over planes side by side, widths that are
+    and are not a strip's multiple, and both paddings."""
+    for shape, padding, seed in (((2, 3, 70, 300), "valid", 31), ((1, 2, 45, 516), "same", 32),
+                                 ((3, 1, 33, 236), "valid", 33), ((1, 1, 12, 12), "same", 34)):
+        say(f"[one-gradient] {path} {dtype} {shape} {padding}")
+        x, y = make_pair(shape, "uniform", 0.1, seed=seed)
+        lb, a1, a2 = RUNNERS[path](x, y, padding, dloss=0.75, dtype=dtype)
+        lx, b1, nb = RUNNERS[path](x, y, padding, dloss=0.75, dtype=dtype, grad2=False)
+        ly, nc, c2 = RUNNERS[path](x, y, padding, dloss=0.75, dtype=dtype, grad1=False)
+        assert nb is None and nc is None
+        assert np.array_equal(b1, a1) and np.array_equal(c2, a2)
+        if path == "loss_and_grad":
+            assert lx == lb and ly == lb
