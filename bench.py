@@ -434,18 +434,19 @@ def one_launch_record(t1, t2, padding, ws, reps):
     return rec
 
 
-def autograd_record(t1, t2, padding, reps):
-    """ssim_loss(img1, img2).backward() with both images requiring
-    gradients, timed three ways: the step as the GPU queue sees it (HIP
-    events around reps steps), the host's time to issue a step (autograd
-    engine and binding; no synchronisation inside the loop) and the GPU time
-    of the step's launches alone, back to back without autograd."""
+def autograd_record(t1, t2, padding, reps, both=True):
+    """ssim_loss(img1, img2).backward() with both images requiring gradients
+    (or img1 alone, as for a render against a fixed ground truth), timed
+    three ways: the step as the GPU queue sees it (HIP events around reps
+    steps), the host's time to issue a step (autograd engine and binding; no
+    synchronisation inside the loop) and the GPU time of the step's launches
+    alone, back to back without autograd."""
     import torch
 
     import ssim_loss_amd as S
 
     a1 = t1.detach().clone().requires_grad_(True)
-    a2 = t2.detach().clone().requires_grad_(True)
+    a2 = t2.detach().clone().requires_grad_(both)
     early = 4 * t1.nbytes <= S.EARLY_GRADIENT_BYTES
 
     def step():
@@ -466,15 +467,16 @@ def autograd_record(t1, t2, padding, reps):
     loss = torch.empty((), dtype=torch.float32, device=dev)
     dl = torch.ones((), dtype=torch.float32, device=dev)
     if early:
-        gbuf = torch.empty((2,) + tuple(t1.shape), dtype=torch.float32, device=dev)
+        gbuf = torch.empty((2 if both else 1,) + tuple(t1.shape), dtype=torch.float32, device=dev)
 
         def kernels():
-            S.ssim_loss_and_grad(t1, t2, padding, dl, loss, ws, gbuf[0], gbuf[1])
+            S.ssim_loss_and_grad(t1, t2, padding, dl, loss, ws, gbuf[0], gbuf[1] if both else None)
             S.ssim_grad_scale(dl, gbuf, gbuf)
 
-        launches = "ssim_loss_and_grad (upstream gradient 1) + one ssim_grad_scale over both"
+        launches = ("ssim_loss_and_grad (upstream gradient 1) + one ssim_grad_scale over "
+                    + ("both" if both else "grad_img1"))
     else:
-        g1, g2 = torch.empty_like(t1), torch.empty_like(t2)
+        g1, g2 = torch.empty_like(t1), (torch.empty_like(t2) if both else None)
 
         def kernels():
             S.ssim_forward(t1, t2, padding, loss, None, ws)
@@ -485,7 +487,7 @@ def autograd_record(t1, t2, padding, reps):
     N, C, H, W = t1.shape
     return {"ms_per_step": round(step_ms, 5), "mpix_per_s": round(N * H * W / (step_ms * 1e-3) / 1e6, 1),
             "host_ms_per_step": round(host_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5),
-            "gradients": "both", "launches": launches, "steps": reps}
+            "gradients": "both" if both else "grad_img1", "launches": launches, "steps": reps}
 
 
 # ---------------------------------------------------------------------------
@@ -932,7 +934,9 @@ def main():
     # size; the default run adds the 4K batch below
     autograd = None
     if args.all_kernels and args.dtype == "float32":
-        autograd = {args.workload: autograd_record(t1, t2, w.padding, min(K, 500))}
+        autograd = {args.workload: autograd_record(t1, t2, w.padding, min(K, 500)),
+                    f"{args.workload}, grad_img1 only":
+                        autograd_record(t1, t2, w.padding, min(K, 500), both=False)}
 
     # cold: flush the 256 MB last-level cache before each step (outside the events)
     cold = None
